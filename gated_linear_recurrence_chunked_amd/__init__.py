@@ -1,0 +1,17 @@
+"""MI355X-native gated linear recurrence (Entangled State Attention hot path).
+
+The compute lives in ``libesa.so`` (hand-written HIP kernels for gfx950 behind a C ABI,
+declared in ``include/esa.h``).  This package is a thin binding: argument marshalling and
+torch-owned device memory only.  Importing it does not load the library; the first call
+does, and fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+__all__ = ["scan_fwd", "scan_bwd", "state_step", "library_path", "load_library"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)
