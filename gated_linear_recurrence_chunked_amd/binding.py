@@ -1,0 +1,226 @@
+"""ctypes binding of libesa.so (include/esa.h), with torch for device memory and streams.
+
+Argument marshalling only: every step of the computation runs in the library's HIP
+kernels.  When the library is missing, every call raises; there is no fallback path.
+
+    y, final_state = scan_fwd(a, v, q, init_state=None, mode="controlled")
+    y, final_state, ckpt = scan_fwd(a, v, q, mode="controlled", return_ckpt=True)
+    da, dv, dq, d_init = scan_bwd(a, v, q, dy, init_state=None, d_final_state=None,
+                                  ckpt=None, mode="controlled")
+    y = state_step(a, v, q, state, mode="controlled")        # state: fp32, updated in place
+
+Sequence tensors are [B, T, H, Dh] (fp32, fp16 or bf16, one dtype per call); states are
+fp32 [B, H, Dh].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libesa.so"
+
+ESA_OK = 0
+STATUS_NAMES = {0: "ESA_OK", 1: "ESA_ERR_INVALID_ARG", 2: "ESA_ERR_UNSUPPORTED",
+                3: "ESA_ERR_WORKSPACE", 4: "ESA_ERR_HIP"}
+DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+MODES = {"direct": 0, "controlled": 1}
+
+# every function include/esa.h declares: name -> (restype, argtypes)
+_P = ctypes.c_void_p
+_I = ctypes.c_int64
+_C = ctypes.c_int
+_Z = ctypes.c_size_t
+SIGNATURES = {
+    "esa_abi_version": (_C, []),
+    "esa_status_string": (ctypes.c_char_p, [_C]),
+    "esa_scan_workspace_bytes": (_Z, [_I, _I, _I, _I, _C]),
+    "esa_scan_ckpt_bytes": (_Z, [_I, _I, _I, _I]),
+    "esa_workspace_init": (_C, [_P, _Z, _P]),
+    "esa_scan_fwd": (_C, [_I, _I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "esa_scan_bwd": (_C, [_I, _I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                          _P, _P, _Z, _P]),
+    "esa_state_step": (_C, [_I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _P]),
+}
+
+_lock = threading.Lock()
+_lib = None
+_workspaces: dict = {}
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, LIB_NAME)
+
+
+def load_library():
+    """Load libesa.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    f"{path} is missing: build it first with "
+                    "`python -m gated_linear_recurrence_chunked_amd.build` (hipcc, gfx950)")
+            lib = ctypes.CDLL(path)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+class EsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = load_library().esa_status_string(status).decode()
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != ESA_OK:
+        raise EsaError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _mode(mode) -> int:
+    if isinstance(mode, str):
+        return MODES[mode]
+    return int(mode)
+
+
+def _seq(name, t, like=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, T, H, Dh], got {tuple(t.shape)}")
+    if t.dtype not in DTYPES:
+        raise TypeError(f"{name}: dtype {t.dtype} not supported")
+    if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device):
+        raise ValueError(f"{name} must match shape/dtype/device of the gate logits")
+    return t.contiguous()
+
+
+def _state(name, t, B, H, Dh, device):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or tuple(t.shape) != (B, H, Dh) or t.device != device:
+        raise ValueError(f"{name} must be fp32 [B, H, Dh] = {(B, H, Dh)} on {device}")
+    return t.contiguous()
+
+
+def workspace_bytes(B, T, H, Dh, dtype) -> int:
+    return int(load_library().esa_scan_workspace_bytes(B, T, H, Dh, DTYPES[dtype]))
+
+
+def ckpt_bytes(B, T, H, Dh) -> int:
+    return int(load_library().esa_scan_ckpt_bytes(B, T, H, Dh))
+
+
+def get_workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-initialised workspace of at least nbytes, cached per (device, stream).
+
+    The library leaves a workspace ready for reuse after every call, so the cache only
+    zero-fills on allocation.  One workspace per stream: calls on one stream are ordered.
+    """
+    dev = torch.device(device)
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def scan_fwd(a, v, q, init_state=None, mode="controlled", return_ckpt=False, final_state=None,
+             y=None, workspace=None):
+    """Forward scan with fused gate and readout (esa_scan_fwd)."""
+    lib = load_library()
+    a = _seq("gate_logit", a)
+    v = _seq("value", v, a)
+    q = _seq("query", q, a)
+    B, T, H, Dh = a.shape
+    init_state = _state("init_state", init_state, B, H, Dh, a.device)
+    if y is None:
+        y = torch.empty_like(a)
+    if final_state is None:
+        final_state = torch.empty((B, H, Dh), dtype=torch.float32, device=a.device)
+    ckpt = None
+    if return_ckpt:
+        nck = max(1, ckpt_bytes(B, T, H, Dh) // 4)
+        ckpt = torch.empty(nck, dtype=torch.float32, device=a.device)
+    need = workspace_bytes(B, T, H, Dh, a.dtype)
+    ws = workspace if workspace is not None else get_workspace(need, a.device)
+    with torch.cuda.device(a.device):
+        st = lib.esa_scan_fwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode), _ptr(a), _ptr(v), _ptr(q),
+                              _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(ckpt), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream_handle(a.device))
+    _check(st, "esa_scan_fwd")
+    if return_ckpt:
+        return y, final_state, ckpt
+    return y, final_state
+
+
+def scan_bwd(a, v, q, dy, init_state=None, d_final_state=None, ckpt=None, mode="controlled",
+             workspace=None):
+    """Backward of scan_fwd (esa_scan_bwd).  Returns (d_logit, d_value, d_query, d_init)."""
+    lib = load_library()
+    a = _seq("gate_logit", a)
+    v = _seq("value", v, a)
+    q = _seq("query", q, a)
+    dy = _seq("dy", dy, a)
+    B, T, H, Dh = a.shape
+    init_state = _state("init_state", init_state, B, H, Dh, a.device)
+    d_final_state = _state("d_final_state", d_final_state, B, H, Dh, a.device)
+    if ckpt is not None:
+        if ckpt.dtype != torch.float32 or ckpt.numel() * 4 < ckpt_bytes(B, T, H, Dh):
+            raise ValueError("ckpt must be the fp32 checkpoint of scan_fwd(return_ckpt=True)")
+        ckpt = ckpt.contiguous()
+    da = torch.empty_like(a)
+    dv = torch.empty_like(a)
+    dq = torch.empty_like(a)
+    d_init = torch.empty((B, H, Dh), dtype=torch.float32, device=a.device)
+    need = workspace_bytes(B, T, H, Dh, a.dtype)
+    ws = workspace if workspace is not None else get_workspace(need, a.device)
+    with torch.cuda.device(a.device):
+        st = lib.esa_scan_bwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode), _ptr(a), _ptr(v), _ptr(q),
+                              _ptr(init_state), _ptr(dy), _ptr(d_final_state), _ptr(ckpt),
+                              _ptr(da), _ptr(dv), _ptr(dq), _ptr(d_init), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream_handle(a.device))
+    _check(st, "esa_scan_bwd")
+    return da, dv, dq, d_init
+
+
+def state_step(a, v, q, state, mode="controlled", y=None):
+    """One-token update (esa_state_step): `state` (fp32 [B, H, Dh]) is updated in place."""
+    lib = load_library()
+    for name, t in (("gate_logit", a), ("value", v), ("query", q)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 3:
+            raise ValueError(f"{name} must be a [B, H, Dh] CUDA (HIP) tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if v.shape != a.shape or q.shape != a.shape or v.dtype != a.dtype or q.dtype != a.dtype:
+        raise ValueError("gate_logit, value and query must share shape and dtype")
+    if a.dtype not in DTYPES:
+        raise TypeError(f"dtype {a.dtype} not supported")
+    B, H, Dh = a.shape
+    if state.dtype != torch.float32 or tuple(state.shape) != (B, H, Dh) or not state.is_contiguous():
+        raise ValueError("state must be a contiguous fp32 [B, H, Dh] tensor")
+    if y is None:
+        y = torch.empty_like(a)
+    with torch.cuda.device(a.device):
+        st = lib.esa_state_step(B, H, Dh, DTYPES[a.dtype], _mode(mode), _ptr(a), _ptr(v), _ptr(q),
+                                _ptr(state), _ptr(y), _stream_handle(a.device))
+    _check(st, "esa_state_step")
+    return y

@@ -1,0 +1,364 @@
+// Host side of libesa.so: argument validation, workspace layout and kernel dispatch over
+// (dtype, mode, Dh).  Every check runs before the first HIP call, so an invalid call
+// changes nothing on the device.  The library allocates nothing and never synchronises.
+#include <stdint.h>
+#include <string.h>
+
+#include "esa.h"
+#include "esa_common.hpp"
+
+using namespace esa;
+
+namespace {
+
+struct Problem {
+    int64_t B, T, H, Dh, C, nLanes, nElem;
+    int dtype, mode;
+    int64_t esize;
+};
+
+struct TileShape {
+    int CB, TTf, TTb;
+};
+
+template <typename T, int DH>
+TileShape tile_shape_of() {
+    return TileShape{FwdCfg<T, DH>::G::CB, FwdCfg<T, DH>::G::TT, BwdCfg<T, DH>::G::TT};
+}
+
+template <typename T>
+TileShape tile_shape_dh(int64_t Dh) {
+    switch (Dh) {
+        case 16: return tile_shape_of<T, 16>();
+        case 32: return tile_shape_of<T, 32>();
+        case 64: return tile_shape_of<T, 64>();
+        default: return tile_shape_of<T, 128>();
+    }
+}
+
+TileShape tile_shape(int dtype, int64_t Dh) {
+    switch (dtype) {
+        case ESA_F32: return tile_shape_dh<float>(Dh);
+        case ESA_F16: return tile_shape_dh<_Float16>(Dh);
+        default: return tile_shape_dh<__bf16>(Dh);
+    }
+}
+
+bool supported_dh(int64_t Dh) { return Dh == 16 || Dh == 32 || Dh == 64 || Dh == 128; }
+
+bool mul64(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_sizes(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode, Problem* pr) {
+    if (dtype < ESA_F32 || dtype > ESA_BF16 || mode < ESA_DIRECT || mode > ESA_CONTROLLED)
+        return ESA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Dh < 1 || T < 0) return ESA_ERR_INVALID_ARG;
+    if (!supported_dh(Dh)) return ESA_ERR_UNSUPPORTED;
+    pr->B = B;
+    pr->T = T;
+    pr->H = H;
+    pr->Dh = Dh;
+    pr->dtype = dtype;
+    pr->mode = mode;
+    pr->esize = dtype == ESA_F32 ? 4 : 2;
+    int64_t bytes;
+    if (!mul64(H, Dh, &pr->C) || !mul64(B, pr->C, &pr->nLanes) || !mul64(pr->nLanes, T, &pr->nElem) ||
+        !mul64(pr->nElem, 4, &bytes) || !mul64(pr->nLanes, 16, &bytes))
+        return ESA_ERR_INVALID_ARG;
+    return ESA_OK;
+}
+
+struct Layout {
+    uint32_t nCB, nTilesF, nTilesB;
+    int64_t nck;
+    size_t offX, offY, offCk, total;
+};
+
+// Workspace: [header 256 B][X words: nTiles x nLanes x 8 B][Y words: same][checkpoint].
+int layout_of(const Problem& pr, Layout* L) {
+    const TileShape ts = tile_shape(pr.dtype, pr.Dh);
+    const int64_t nCB = cdiv(pr.nLanes, ts.CB);
+    const int64_t nTF = pr.T > 0 ? cdiv(pr.T, ts.TTf) : 0;
+    const int64_t nTB = pr.T > 0 ? cdiv(pr.T, ts.TTb) : 0;
+    const int64_t nTM = nTF > nTB ? nTF : nTB;
+    int64_t nwg, words, xbytes, ckbytes;
+    if (!mul64(nCB, nTM, &nwg) || nwg > (int64_t)UINT32_MAX || nCB > (int64_t)UINT32_MAX)
+        return ESA_ERR_UNSUPPORTED;
+    if (!mul64(nTM, pr.nLanes, &words) || !mul64(words, 8, &xbytes)) return ESA_ERR_UNSUPPORTED;
+    L->nCB = (uint32_t)nCB;
+    L->nTilesF = (uint32_t)nTF;
+    L->nTilesB = (uint32_t)nTB;
+    L->nck = cdiv(pr.T, kCkptChunk);
+    if (!mul64(L->nck, pr.nLanes, &ckbytes) || !mul64(ckbytes, 4, &ckbytes)) return ESA_ERR_UNSUPPORTED;
+    L->offX = 256;
+    L->offY = L->offX + align256((size_t)xbytes);
+    L->offCk = L->offY + align256((size_t)xbytes);
+    L->total = L->offCk + align256((size_t)ckbytes);
+    return ESA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    const void* p;
+    size_t n;
+};
+
+bool overlap(const Range& x, const Range& y) {
+    if (!x.p || !y.p || x.n == 0 || y.n == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(x.p), b0 = reinterpret_cast<uintptr_t>(y.p);
+    return a0 < b0 + y.n && b0 < a0 + x.n;
+}
+
+// true if any output overlaps any input or another output
+bool any_overlap(const Range* in, int nin, const Range* out, int nout) {
+    for (int i = 0; i < nout; ++i) {
+        for (int k = 0; k < nin; ++k)
+            if (overlap(out[i], in[k])) return true;
+        for (int k = i + 1; k < nout; ++k)
+            if (overlap(out[i], out[k])) return true;
+    }
+    return false;
+}
+
+#define ESA_DISPATCH(KIND, dtype, mode, Dh, params, stream)                                   \
+    [&]() -> hipError_t {                                                                     \
+        switch (dtype * 2 + mode) {                                                           \
+            case ESA_F32 * 2 + 0: return KIND##_dh<float, 0>(Dh, params, stream);            \
+            case ESA_F32 * 2 + 1: return KIND##_dh<float, 1>(Dh, params, stream);            \
+            case ESA_F16 * 2 + 0: return KIND##_dh<_Float16, 0>(Dh, params, stream);         \
+            case ESA_F16 * 2 + 1: return KIND##_dh<_Float16, 1>(Dh, params, stream);         \
+            case ESA_BF16 * 2 + 0: return KIND##_dh<__bf16, 0>(Dh, params, stream);          \
+            default: return KIND##_dh<__bf16, 1>(Dh, params, stream);                        \
+        }                                                                                     \
+    }()
+
+template <typename T, int M>
+hipError_t fwd_dh(int64_t Dh, const FwdParams& p, hipStream_t s) {
+    switch (Dh) {
+        case 16: return launch_fwd<T, M, 16>(p, s);
+        case 32: return launch_fwd<T, M, 32>(p, s);
+        case 64: return launch_fwd<T, M, 64>(p, s);
+        default: return launch_fwd<T, M, 128>(p, s);
+    }
+}
+template <typename T, int M>
+hipError_t bwd_dh(int64_t Dh, const BwdParams& p, hipStream_t s) {
+    switch (Dh) {
+        case 16: return launch_bwd<T, M, 16>(p, s);
+        case 32: return launch_bwd<T, M, 32>(p, s);
+        case 64: return launch_bwd<T, M, 64>(p, s);
+        default: return launch_bwd<T, M, 128>(p, s);
+    }
+}
+template <typename T, int M>
+hipError_t step_dh(int64_t Dh, const StepParams& p, hipStream_t s) {
+    switch (Dh) {
+        case 16: return launch_step<T, M, 16>(p, s);
+        case 32: return launch_step<T, M, 32>(p, s);
+        case 64: return launch_step<T, M, 64>(p, s);
+        default: return launch_step<T, M, 128>(p, s);
+    }
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ESA_OK : ESA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int esa_abi_version(void) { return ESA_ABI_VERSION; }
+
+const char* esa_status_string(int status) {
+    switch (status) {
+        case ESA_OK: return "ESA_OK: success";
+        case ESA_ERR_INVALID_ARG:
+            return "ESA_ERR_INVALID_ARG: null pointer, bad size or enum, misaligned or overlapping buffer";
+        case ESA_ERR_UNSUPPORTED: return "ESA_ERR_UNSUPPORTED: Dh not in {16, 32, 64, 128} or problem too large";
+        case ESA_ERR_WORKSPACE: return "ESA_ERR_WORKSPACE: workspace missing or smaller than esa_scan_workspace_bytes()";
+        case ESA_ERR_HIP: return "ESA_ERR_HIP: the HIP runtime rejected a kernel launch";
+        default: return "unknown esa_status";
+    }
+}
+
+size_t esa_scan_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype) {
+    Problem pr;
+    if (check_sizes(B, T, H, Dh, dtype, ESA_DIRECT, &pr) != ESA_OK) return 0;
+    Layout L;
+    if (layout_of(pr, &L) != ESA_OK) return 0;
+    return L.total;
+}
+
+size_t esa_scan_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t Dh) {
+    Problem pr;
+    if (check_sizes(B, T, H, Dh, ESA_F32, ESA_DIRECT, &pr) != ESA_OK) return 0;
+    int64_t n;
+    if (!mul64(cdiv(T, kCkptChunk), pr.nLanes, &n) || !mul64(n, 4, &n)) return 0;
+    return (size_t)n;
+}
+
+int esa_workspace_init(void* workspace, size_t bytes, void* stream) {
+    if (!workspace || !aligned16(workspace)) return ESA_ERR_INVALID_ARG;
+    return hip_status(launch_fill_zero(workspace, bytes, (hipStream_t)stream));
+}
+
+int esa_scan_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
+                 const void* gate_logit, const void* value, const void* query,
+                 const float* init_state, void* y, float* final_state, float* ckpt,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    Problem pr;
+    int rc = check_sizes(B, T, H, Dh, dtype, mode, &pr);
+    if (rc != ESA_OK) return rc;
+    if (T > 0 && (!gate_logit || !value || !query || !y)) return ESA_ERR_INVALID_ARG;
+    const void* ptrs[] = {gate_logit, value, query, init_state, y, final_state, ckpt, workspace};
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return ESA_ERR_INVALID_ARG;
+    Layout L;
+    rc = layout_of(pr, &L);
+    if (rc != ESA_OK) return rc;
+    const size_t seq = (size_t)(pr.nElem * pr.esize), st = (size_t)(pr.nLanes * 4);
+    const size_t ckb = esa_scan_ckpt_bytes(B, T, H, Dh);
+    const Range in[] = {{gate_logit, seq}, {value, seq}, {query, seq},
+                        {init_state == final_state ? nullptr : init_state, st}};
+    const Range out[] = {{y, seq}, {final_state, st}, {ckpt, ckb}, {workspace, workspace_bytes}};
+    if (any_overlap(in, 4, out, 4)) return ESA_ERR_INVALID_ARG;
+    if (T > 0 && (!workspace || workspace_bytes < L.total)) return ESA_ERR_WORKSPACE;
+
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (final_state && final_state != init_state)
+            return hip_status(launch_copy_f32(final_state, init_state, pr.nLanes, s));
+        return ESA_OK;
+    }
+    char* ws = static_cast<char*>(workspace);
+    FwdParams p;
+    p.a = gate_logit;
+    p.v = value;
+    p.q = query;
+    p.e0 = init_state;
+    p.y = y;
+    p.eT = final_state;
+    p.ckpt = ckpt;
+    p.hdr = reinterpret_cast<uint32_t*>(ws);
+    p.flagX = reinterpret_cast<uint64_t*>(ws + L.offX);
+    p.flagY = reinterpret_cast<uint64_t*>(ws + L.offY);
+    p.T = pr.T;
+    p.C = pr.C;
+    p.nLanes = pr.nLanes;
+    p.nck = L.nck;
+    p.nCB = L.nCB;
+    p.nTiles = L.nTilesF;
+    p.nWG = L.nCB * L.nTilesF;
+    return hip_status(ESA_DISPATCH(fwd, dtype, mode, Dh, p, s));
+}
+
+int esa_scan_bwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
+                 const void* gate_logit, const void* value, const void* query,
+                 const float* init_state, const void* dy, const float* d_final_state,
+                 const float* ckpt, void* d_gate_logit, void* d_value, void* d_query,
+                 float* d_init_state, void* workspace, size_t workspace_bytes, void* stream) {
+    Problem pr;
+    int rc = check_sizes(B, T, H, Dh, dtype, mode, &pr);
+    if (rc != ESA_OK) return rc;
+    if (T > 0 && (!gate_logit || !value || !query || !dy || !d_gate_logit || !d_value || !d_query))
+        return ESA_ERR_INVALID_ARG;
+    const void* ptrs[] = {gate_logit, value, query, init_state, dy, d_final_state, ckpt,
+                          d_gate_logit, d_value, d_query, d_init_state, workspace};
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return ESA_ERR_INVALID_ARG;
+    Layout L;
+    rc = layout_of(pr, &L);
+    if (rc != ESA_OK) return rc;
+    const size_t seq = (size_t)(pr.nElem * pr.esize), st = (size_t)(pr.nLanes * 4);
+    const size_t ckb = esa_scan_ckpt_bytes(B, T, H, Dh);
+    const Range in[] = {{gate_logit, seq}, {value, seq}, {query, seq}, {init_state, st},
+                        {dy, seq}, {d_final_state, st}, {ckpt, ckb}};
+    const Range out[] = {{d_gate_logit, seq}, {d_value, seq}, {d_query, seq}, {d_init_state, st},
+                         {workspace, workspace_bytes}};
+    if (any_overlap(in, 7, out, 5)) return ESA_ERR_INVALID_ARG;
+    if (T > 0 && (!workspace || workspace_bytes < L.total)) return ESA_ERR_WORKSPACE;
+
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (d_init_state) return hip_status(launch_copy_f32(d_init_state, d_final_state, pr.nLanes, s));
+        return ESA_OK;
+    }
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* hdr = reinterpret_cast<uint32_t*>(ws);
+    uint64_t* fx = reinterpret_cast<uint64_t*>(ws + L.offX);
+    uint64_t* fy = reinterpret_cast<uint64_t*>(ws + L.offY);
+    const float* ck = ckpt;
+    if (!ck) {
+        // no checkpoint from the caller: one state-only forward pass into the workspace
+        FwdParams f;
+        memset(&f, 0, sizeof(f));
+        f.a = gate_logit;
+        f.v = value;
+        f.e0 = init_state;
+        f.ckpt = reinterpret_cast<float*>(ws + L.offCk);
+        f.hdr = hdr;
+        f.flagX = fx;
+        f.flagY = fy;
+        f.T = pr.T;
+        f.C = pr.C;
+        f.nLanes = pr.nLanes;
+        f.nck = L.nck;
+        f.nCB = L.nCB;
+        f.nTiles = L.nTilesF;
+        f.nWG = L.nCB * L.nTilesF;
+        rc = hip_status(ESA_DISPATCH(fwd, dtype, mode, Dh, f, s));
+        if (rc != ESA_OK) return rc;
+        ck = f.ckpt;
+    }
+    BwdParams p;
+    p.a = gate_logit;
+    p.v = value;
+    p.q = query;
+    p.dy = dy;
+    p.e0 = init_state;
+    p.dET = d_final_state;
+    p.ckpt = ck;
+    p.da = d_gate_logit;
+    p.dv = d_value;
+    p.dq = d_query;
+    p.de0 = d_init_state;
+    p.hdr = hdr;
+    p.flagX = fx;
+    p.flagY = fy;
+    p.T = pr.T;
+    p.C = pr.C;
+    p.nLanes = pr.nLanes;
+    p.nck = L.nck;
+    p.nCB = L.nCB;
+    p.nTiles = L.nTilesB;
+    p.nWG = L.nCB * L.nTilesB;
+    return hip_status(ESA_DISPATCH(bwd, dtype, mode, Dh, p, s));
+}
+
+int esa_state_step(int64_t B, int64_t H, int64_t Dh, int dtype, int mode, const void* gate_logit,
+                   const void* value, const void* query, float* state, void* y, void* stream) {
+    Problem pr;
+    int rc = check_sizes(B, 1, H, Dh, dtype, mode, &pr);
+    if (rc != ESA_OK) return rc;
+    if (!gate_logit || !value || !query || !state || !y) return ESA_ERR_INVALID_ARG;
+    const void* ptrs[] = {gate_logit, value, query, state, y};
+    for (const void* q : ptrs)
+        if (!aligned16(q)) return ESA_ERR_INVALID_ARG;
+    const size_t tok = (size_t)(pr.nLanes * pr.esize), st = (size_t)(pr.nLanes * 4);
+    const Range in[] = {{gate_logit, tok}, {value, tok}, {query, tok}};
+    const Range out[] = {{state, st}, {y, tok}};
+    if (any_overlap(in, 3, out, 2)) return ESA_ERR_INVALID_ARG;
+    StepParams p;
+    p.a = gate_logit;
+    p.v = value;
+    p.q = query;
+    p.state = state;
+    p.y = y;
+    p.nLanes = pr.nLanes;
+    return hip_status(ESA_DISPATCH(step, dtype, mode, Dh, p, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,346 @@
+// Shared definitions of the gfx950 kernels and the host dispatcher of libesa.so.
+//
+// The kernels scan E_t = A_t * E_{t-1} + B_t over T for every (b, h, d) lane of a
+// [B, T, H, Dh] problem (page "Entangled State Attention v2.1", introduction; gates and
+// readout from page "entangled-state-attention 0.1.0", "Core idea").  The scan is an exact
+// re-association of the sequential loop through the pair combine
+// (P1, E1) o (P2, E2) = (P1 P2, E2 + P2 E1) (page "Entangled State Attention",
+// "[ ARCHITECTURE ]", associative composition):
+//
+//   lanes    a thread owns VEC channels (16 bytes of storage) of one (b, t); CB channels
+//            (whole heads, at least 64) form a channel block, NCL = CB / VEC threads wide.
+//   tile     a workgroup owns one channel block over TT = S * L time steps: S time slots
+//            of L consecutive steps, one slot per row of NCL threads.
+//   level 1  each thread folds its L steps in registers into one pair per channel.
+//   level 2  slot pairs go through LDS; one wave scans them in order, lane = channel.
+//   level 3  tiles of one channel block are chained by a decoupled look-back: a tile
+//            publishes its aggregate pair, then walks back over earlier tiles' published
+//            pairs until it meets an inclusive value, then publishes its own inclusive
+//            value.  Workgroups take tiles in ticket order (an atomic counter), so a tile
+//            only ever waits on tiles that are already running.
+//
+// Look-back words are 64-bit (tag, fp32 value) pairs written and read with single-copy
+// atomic 64-bit accesses at agent scope, so no fence is needed between a value and its
+// flag.  The tag carries the call's epoch, so stale words from earlier calls never match
+// and the flag array needs no clearing between calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace esa {
+
+constexpr int kWave = 64;
+constexpr int kCkptChunk = 64;  // state checkpoint every 64 steps
+constexpr float kEps = 1e-6f;   // RMSNorm epsilon (fixed reading of the pages' Norm)
+constexpr int kDirect = 0;
+constexpr int kControlled = 1;
+
+template <typename T>
+struct Storage;
+template <>
+struct Storage<float> {
+    static constexpr int VEC = 4;
+};
+template <>
+struct Storage<_Float16> {
+    static constexpr int VEC = 8;
+};
+template <>
+struct Storage<__bf16> {
+    static constexpr int VEC = 8;
+};
+
+// Tile geometry of a scan kernel instance.
+template <typename T, int DH, int L, int NT>
+struct Geom {
+    static constexpr int VEC = Storage<T>::VEC;
+    static constexpr int CB = DH > 64 ? DH : 64;  // channels per block (whole heads)
+    static constexpr int NCL = CB / VEC;          // threads across one time row
+    static constexpr int S = NT / NCL;            // time slots per tile
+    static constexpr int TT = S * L;              // time steps per tile
+    static constexpr int HL = DH / VEC;           // threads per head
+    static constexpr int CPL = CB / kWave;        // channels per lane of the scan wave
+    static_assert(CB % VEC == 0 && NT % NCL == 0 && S >= 1, "bad tile geometry");
+    static_assert(HL >= 1 && (HL & (HL - 1)) == 0 && HL <= kWave, "head must be 2^k lanes");
+};
+
+// Per-(dtype, Dh) launch configuration of the forward and backward scans.
+template <typename T, int DH>
+struct FwdCfg {
+    static constexpr int NT = 256;
+    static constexpr int L = 4;
+    using G = Geom<T, DH, L, NT>;
+};
+template <typename T, int DH>
+struct BwdCfg {
+    static constexpr int NT = 256;
+    static constexpr int S0 = Geom<T, DH, 1, NT>::S;
+    // the backward tile must start on a checkpoint boundary: TT % 64 == 0
+    static constexpr int L = S0 >= 32 ? 2 : kCkptChunk / S0;
+    using G = Geom<T, DH, L, NT>;
+    static_assert(G::TT % kCkptChunk == 0, "backward tile must be a multiple of 64 steps");
+};
+
+// Workspace layout: [header 256 B][flag X words][flag Y words][internal checkpoint].
+struct WsHeader {
+    uint32_t ticket;  // next tile ticket of the running kernel (self-resetting)
+    uint32_t done;    // workgroups finished (self-resetting)
+    uint32_t epoch;   // incremented by the last workgroup of every scan kernel
+    uint32_t abort;   // sticky: set when a look-back wait timed out (results are NaN)
+    uint32_t pad[60];
+};
+static_assert(sizeof(WsHeader) == 256, "header must be 256 bytes");
+
+constexpr uint32_t kTagAgg = 1u;
+constexpr uint32_t kTagInc = 2u;
+
+struct FwdParams {
+    const void* a;
+    const void* v;
+    const void* q;   // NULL: no readout (checkpoint-only pass)
+    const float* e0;  // NULL: zero initial state
+    void* y;          // NULL: no readout
+    float* eT;
+    float* ckpt;
+    uint32_t* hdr;
+    uint64_t* flagX;
+    uint64_t* flagY;
+    int64_t T;
+    int64_t C;       // H * Dh
+    int64_t nLanes;  // B * C
+    int64_t nck;     // ceil(T / 64)
+    uint32_t nCB;
+    uint32_t nTiles;
+    uint32_t nWG;
+};
+
+struct BwdParams {
+    const void* a;
+    const void* v;
+    const void* q;
+    const void* dy;
+    const float* e0;
+    const float* dET;
+    const float* ckpt;
+    void* da;
+    void* dv;
+    void* dq;
+    float* de0;
+    uint32_t* hdr;
+    uint64_t* flagX;
+    uint64_t* flagY;
+    int64_t T;
+    int64_t C;
+    int64_t nLanes;
+    int64_t nck;
+    uint32_t nCB;
+    uint32_t nTiles;
+    uint32_t nWG;
+};
+
+struct StepParams {
+    const void* a;
+    const void* v;
+    const void* q;
+    float* state;
+    void* y;
+    int64_t nLanes;
+};
+
+// Host-visible launchers, explicitly instantiated in the kernel translation units.
+template <typename T, int MODE, int DH>
+hipError_t launch_fwd(const FwdParams& p, hipStream_t s);
+template <typename T, int MODE, int DH>
+hipError_t launch_bwd(const BwdParams& p, hipStream_t s);
+template <typename T, int MODE, int DH>
+hipError_t launch_step(const StepParams& p, hipStream_t s);
+hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);
+
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+
+// ---------------------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------------------
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+
+// 16 bytes of storage -> VEC fp32 values (exact).
+template <typename T>
+__device__ __forceinline__ void unpack(const uint4& r, float* out);
+template <>
+__device__ __forceinline__ void unpack<float>(const uint4& r, float* out) {
+    out[0] = __uint_as_float(r.x);
+    out[1] = __uint_as_float(r.y);
+    out[2] = __uint_as_float(r.z);
+    out[3] = __uint_as_float(r.w);
+}
+template <>
+__device__ __forceinline__ void unpack<_Float16>(const uint4& r, float* out) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        half2_t h = __builtin_bit_cast(half2_t, w[k]);
+        out[2 * k] = (float)h.x;
+        out[2 * k + 1] = (float)h.y;
+    }
+}
+template <>
+__device__ __forceinline__ void unpack<__bf16>(const uint4& r, float* out) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        out[2 * k] = __uint_as_float(w[k] << 16);
+        out[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+}
+
+// VEC fp32 values -> 16 bytes of storage (round to nearest even).
+template <typename T>
+__device__ __forceinline__ uint4 pack(const float* x);
+template <>
+__device__ __forceinline__ uint4 pack<float>(const float* x) {
+    return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                      __float_as_uint(x[3]));
+}
+template <>
+__device__ __forceinline__ uint4 pack<_Float16>(const float* x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        half2_t h = {(_Float16)x[2 * k], (_Float16)x[2 * k + 1]};
+        w[k] = __builtin_bit_cast(uint32_t, h);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+template <>
+__device__ __forceinline__ uint4 pack<__bf16>(const float* x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        bf2_t h = {(__bf16)x[2 * k], (__bf16)x[2 * k + 1]};
+        w[k] = __builtin_bit_cast(uint32_t, h);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint4 ld16(const void* base, int64_t elem_off, int esize) {
+    const char* p = static_cast<const char*>(base) + elem_off * esize;
+    return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void st16(void* base, int64_t elem_off, int esize, const uint4& v) {
+    char* p = static_cast<char*>(base) + elem_off * esize;
+    *reinterpret_cast<uint4*>(p) = v;
+}
+
+// Gate: s = sigma(a) = 1 / (1 + exp(-a)) and u = 1 - s = sigma(-a), taken as exp(-a) * s so
+// that it keeps full relative precision when s is close to 1.  exp(-a) is capped at 2^126 so
+// that 1 + exp(-a) stays finite (for a < -87 the true s is below 2^-126 and 2^-126 is used);
+// a NaN logit stays NaN.
+__device__ __forceinline__ void gate(float a, float& s, float& u) {
+    float x = a * -1.4426950408889634f;  // -a * log2(e)
+    x = x > 126.0f ? 126.0f : x;
+    const float e = __builtin_amdgcn_exp2f(x);
+    s = __builtin_amdgcn_rcpf(1.0f + e);
+    u = e * s;
+}
+
+// Sum over the HL consecutive, aligned threads that hold one head (a butterfly, so every
+// thread of the head receives the total).
+template <int HL>
+__device__ __forceinline__ float head_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < HL; m <<= 1) x += __shfl_xor(x, m, kWave);
+    return x;
+}
+
+__device__ __forceinline__ uint64_t tag_word(uint32_t tag, float v) {
+    return (static_cast<uint64_t>(tag) << 32) | static_cast<uint64_t>(__float_as_uint(v));
+}
+__device__ __forceinline__ void publish(uint64_t* p, uint32_t tag, float v) {
+    __hip_atomic_store(p, tag_word(tag, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t peek(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t word_tag(uint64_t w) { return static_cast<uint32_t>(w >> 32); }
+__device__ __forceinline__ float word_val(uint64_t w) {
+    return __uint_as_float(static_cast<uint32_t>(w));
+}
+
+// Decoupled look-back over one channel's chain of tiles.  `step` is -1 (walk toward earlier
+// tiles, forward scan) or +1 (toward later tiles, reverse scan).  Returns the carry entering
+// tile `tile`: the composition of the published pairs, ended by an inclusive value.
+//
+// The wait is bounded: after kSpinLimit polls without progress the workgroup raises the
+// sticky abort word of the workspace header and returns NaN, and every other waiting
+// workgroup that sees the abort word returns NaN too, so a broken chain drains instead of
+// hanging.  A correct run never comes near the limit (about a second of polling).
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+__device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t* flagY,
+                                           int64_t nLanes, int64_t lane, int64_t tile, int step,
+                                           uint32_t tagAgg, uint32_t tagInc, uint32_t* hdr) {
+    float ap = 1.0f, ae = 0.0f;
+    int64_t j = tile + step;
+    uint32_t polls = 0;
+    for (;;) {
+        const uint64_t x = peek(flagX + j * nLanes + lane);
+        const uint32_t tg = word_tag(x);
+        if (tg == tagInc) return ae + ap * word_val(x);
+        if (tg == tagAgg) {
+            const uint64_t yv = peek(flagY + j * nLanes + lane);
+            if (word_tag(yv) == tagAgg) {
+                ae = ae + ap * word_val(x);
+                ap = ap * word_val(yv);
+                j += step;
+                continue;
+            }
+        }
+        ++polls;
+        if ((polls & 255u) == 0u) {
+            if (__hip_atomic_load(&hdr[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+                return __builtin_nanf("");
+            if (polls >= kSpinLimit) {
+                __hip_atomic_store(&hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return __builtin_nanf("");
+            }
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// Ticket and epoch of this workgroup; called by all threads (contains a barrier).
+__device__ __forceinline__ void take_ticket(uint32_t* hdr, uint32_t& ticket, uint32_t& epoch) {
+    __shared__ uint32_t sT, sE;
+    if (threadIdx.x == 0) {
+        sT = __hip_atomic_fetch_add(&hdr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sE = __hip_atomic_load(&hdr[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    ticket = sT;
+    epoch = sE;
+}
+
+// Called by one thread at the very end of every workgroup: the last one resets the ticket
+// and done counters and advances the epoch for the next call.
+__device__ __forceinline__ void finish_workgroup(uint32_t* hdr, uint32_t nWG, uint32_t epoch) {
+    const uint32_t d =
+        __hip_atomic_fetch_add(&hdr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == nWG - 1) {
+        __hip_atomic_store(&hdr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&hdr[2], (epoch + 1u) & 0x3fffffffu, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+__device__ __forceinline__ uint32_t make_tag(uint32_t epoch, uint32_t kind) {
+    return (epoch << 2) | kind;
+}
+
+#endif  // device compile
+
+}  // namespace esa

@@ -1,0 +1,143 @@
+/*
+ * esa.h - C ABI of libesa.so: the gated linear recurrence of Entangled State Attention (ESA)
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "entangled-state-attention 0.1.0", section "Core idea"; page
+ * "Entangled State Attention v2.1", introduction; page "Entangled State Attention",
+ * section "[ ARCHITECTURE ]"):
+ *
+ *   s_t = sigma(a_t)                                     gate from the gate logit a_t
+ *   direct:      E_t = s_t * E_{t-1} + v_t               (A = sigma(a), B = V)
+ *   controlled:  E_t = s_t * E_{t-1} + (1 - s_t) * v_t   (g = sigma(a), B = (1 - g) V)
+ *   y_t = q_t * E_t / sqrt(mean_h(E_t^2) + 1e-6)         readout, per head over Dh channels
+ *
+ * elementwise for every (batch b, head h, channel d) lane and causal over t.  The pages
+ * leave "Norm" undefined; this library reads it as per-head RMSNorm with eps = 1e-6 inside
+ * the square root and no gain.  The projections x W_A, x W_V, x W_Q and the output
+ * projection W_O are outside the library: it takes the gate logits, values and queries.
+ *
+ * Layout.  Sequence tensors are contiguous [B, T, H, Dh] with Dh fastest, in the storage
+ * dtype.  States are contiguous [B, H, Dh] and always fp32.  All arithmetic is fp32 with
+ * fp32 accumulation; outputs in a 16-bit dtype are rounded to nearest even.
+ *
+ * Ownership and execution.  The caller owns every buffer (device memory).  The library
+ * never allocates, frees or synchronises; each call validates its arguments on the host,
+ * enqueues its kernels on `stream` (a hipStream_t; NULL is the default stream) and
+ * returns.  Errors that occur while the kernels run surface at the caller's next
+ * synchronisation.  The library holds no global state and is reentrant, but calls that
+ * share one workspace must not run concurrently (use one workspace per stream).
+ *
+ * Errors.  Every entry point returns an esa_status.  All argument checks run before any
+ * HIP call, so an invalid call changes nothing on the device:
+ *   ESA_ERR_INVALID_ARG  null required pointer, negative size, bad enum, pointer not
+ *                        16-byte aligned, element count overflowing int64, or an output
+ *                        that overlaps an input
+ *   ESA_ERR_UNSUPPORTED  Dh not in {16, 32, 64, 128}, or a problem whose tile count
+ *                        exceeds 2^32 - 1
+ *   ESA_ERR_WORKSPACE    workspace NULL or smaller than esa_scan_workspace_bytes()
+ *   ESA_ERR_HIP          a kernel launch was rejected by the HIP runtime
+ */
+#ifndef ESA_H
+#define ESA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ESA_ABI_VERSION 1
+
+/* Checkpoint granularity: the forward can store the fp32 state at every 64th step. */
+#define ESA_CKPT_CHUNK 64
+
+typedef enum {
+    ESA_OK = 0,
+    ESA_ERR_INVALID_ARG = 1,
+    ESA_ERR_UNSUPPORTED = 2,
+    ESA_ERR_WORKSPACE = 3,
+    ESA_ERR_HIP = 4
+} esa_status;
+
+/* Storage dtype of the sequence tensors (precision modes of page "Entangled State
+ * Attention v2.1", section "3. Precision": fp16 default, bf16, fp32). */
+typedef enum { ESA_F32 = 0, ESA_F16 = 1, ESA_BF16 = 2 } esa_dtype;
+
+/* Recurrence form (page "entangled-state-attention 0.1.0", "Direct vs controlled mode"). */
+typedef enum { ESA_DIRECT = 0, ESA_CONTROLLED = 1 } esa_mode;
+
+/* ABI version of the loaded library (ESA_ABI_VERSION at build time). */
+int esa_abi_version(void);
+
+/* Static, human-readable text for a status code; never NULL. */
+const char *esa_status_string(int status);
+
+/* Bytes of device workspace that esa_scan_fwd / esa_scan_bwd need for this problem.  One
+ * workspace sized for the largest problem serves every smaller one.  Returns 0 for
+ * invalid or unsupported sizes.  A workspace must be zero-filled once before its first use
+ * (hipMemset, torch.zeros, or esa_workspace_init); every call that completes leaves it
+ * ready for the next call. */
+size_t esa_scan_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype);
+
+/* Bytes of the forward's checkpoint: fp32 [B, ceil(T / 64), H, Dh], the state E_t at
+ * t = 64 k + 63 for each chunk k (the last chunk holds E_{T-1}).  Returns 0 on bad sizes. */
+size_t esa_scan_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t Dh);
+
+/* Zero-fills `bytes` of workspace on `stream` (a fill kernel, safe inside graph capture). */
+int esa_workspace_init(void *workspace, size_t bytes, void *stream);
+
+/* Forward scan with fused gate and readout: prefill and training forward (page "Entangled
+ * State Attention", "[ ARCHITECTURE ]": associative composition over the sequence, then a
+ * compact final state; "[ QUICK START ]": esa.prefill returns the output and the state).
+ *   B, T, H, Dh   sizes; T = 0 is allowed: only final_state is written, and the sequence
+ *                 pointers may then be NULL
+ *   dtype, mode   esa_dtype, esa_mode
+ *   gate_logit    [B,T,H,Dh] dtype, in: a_t
+ *   value         [B,T,H,Dh] dtype, in: v_t
+ *   query         [B,T,H,Dh] dtype, in: q_t
+ *   init_state    [B,H,Dh] fp32, in, or NULL for E_{-1} = 0
+ *   y             [B,T,H,Dh] dtype, out: y_t
+ *   final_state   [B,H,Dh] fp32, out (E_{T-1}), or NULL; may equal init_state (in place)
+ *   ckpt          esa_scan_ckpt_bytes() fp32, out (for esa_scan_bwd), or NULL
+ *   workspace     device buffer of workspace_bytes >= esa_scan_workspace_bytes()
+ *   stream        hipStream_t or NULL */
+int esa_scan_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
+                 const void *gate_logit, const void *value, const void *query,
+                 const float *init_state, void *y, float *final_state, float *ckpt,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward of esa_scan_fwd: the chain rule through readout, recurrence and gate, run as a
+ * reverse-time scan dE_t = gE_t + s_{t+1} dE_{t+1} (no page states it; it is derived from
+ * the forward of page "entangled-state-attention 0.1.0", "Core idea").
+ *   gate_logit, value, query, init_state   the forward's inputs (init_state may be NULL)
+ *   dy             [B,T,H,Dh] dtype, in: gradient of y
+ *   d_final_state  [B,H,Dh] fp32, in: gradient of final_state, or NULL for zero
+ *   ckpt           the forward's checkpoint, or NULL (the library then recomputes it into
+ *                  the workspace with one extra pass that reads a and v)
+ *   d_gate_logit, d_value, d_query  [B,T,H,Dh] dtype, out
+ *   d_init_state   [B,H,Dh] fp32, out, or NULL
+ * T = 0 is allowed: d_init_state receives d_final_state (or zeros), and the sequence
+ * pointers may then be NULL. */
+int esa_scan_bwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
+                 const void *gate_logit, const void *value, const void *query,
+                 const float *init_state, const void *dy, const float *d_final_state,
+                 const float *ckpt, void *d_gate_logit, void *d_value, void *d_query,
+                 float *d_init_state, void *workspace, size_t workspace_bytes, void *stream);
+
+/* One-token recurrent update with readout, for generation (page "Entangled State
+ * Attention", "[ ARCHITECTURE ]" one-token update and "[ QUICK START ]" esa.decode_step;
+ * page "Entangled State Attention v2.1", section 5, lightning_step):
+ *   gate_logit, value, query   [B,H,Dh] dtype, in: this token's a, v, q
+ *   state                      [B,H,Dh] fp32, in/out, updated in place
+ *   y                          [B,H,Dh] dtype, out
+ * Needs no workspace. */
+int esa_state_step(int64_t B, int64_t H, int64_t Dh, int dtype, int mode,
+                   const void *gate_logit, const void *value, const void *query, float *state,
+                   void *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ESA_H */

@@ -1,0 +1,42 @@
+"""Shared test helpers: the parity error metric and tolerances.
+
+The error of a result x against the oracle's r is
+
+    err = max_i |x_i - r_i| / max(|r_i|, rms(r))
+
+an elementwise relative error wherever |r_i| >= rms(r), and an absolute error scaled by
+rms(r) below it.  A pure elementwise ratio is undefined where r_i = 0 and unbounded near
+it, and the states and gradients here are signed sums that cancel.  The bar is 1e-5 for
+fp32 inputs and 5e-3 for fp16 / bf16 inputs.
+"""
+import numpy as np
+import torch
+
+TOL = {torch.float32: 1e-5, torch.float16: 5e-3, torch.bfloat16: 5e-3}
+
+
+def f64(x):
+    if isinstance(x, torch.Tensor):
+        return x.detach().to("cpu").double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def err(x, r) -> float:
+    x = f64(x)
+    r = f64(r)
+    assert x.shape == r.shape, (x.shape, r.shape)
+    if r.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(x)):
+        return float("inf")
+    rms = float(np.sqrt(np.mean(r * r)))
+    scale = np.maximum(np.abs(r), rms)
+    scale = np.where(scale > 0, scale, 1.0)
+    return float(np.max(np.abs(x - r) / scale))
+
+
+def assert_close(name, x, r, dtype):
+    e = err(x, r)
+    tol = TOL[dtype]
+    assert e <= tol, f"{name}: err {e:.3e} > tol {tol:.0e}"
+    return e

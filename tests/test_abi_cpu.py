@@ -1,0 +1,141 @@
+"""The C-ABI library on the host: it loads, exports every function include/esa.h declares,
+and rejects bad arguments with the documented status codes before any HIP call.
+
+No test here launches a kernel: every call below fails validation, which returns before
+the first HIP runtime call.  Pointers are never dereferenced on the host, so the fake but
+aligned addresses used here are safe.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_linear_recurrence_chunked_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "esa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(esa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        pytest.skip("libesa.so not built")
+    return binding.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"esa_scan_fwd", "esa_scan_bwd", "esa_state_step"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in binding.SIGNATURES, n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.esa_abi_version() == 1
+    for s in range(5):
+        assert lib.esa_status_string(s).decode().startswith(
+            ["ESA_OK", "ESA_ERR_INVALID_ARG", "ESA_ERR_UNSUPPORTED", "ESA_ERR_WORKSPACE",
+             "ESA_ERR_HIP"][s])
+    assert lib.esa_status_string(99)
+
+
+def test_workspace_and_ckpt_sizes(lib):
+    ws = lib.esa_scan_workspace_bytes
+    assert ws(1, 256, 2, 16, 0) > 256
+    assert ws(64, 65536, 8, 64, 1) > ws(16, 8192, 8, 64, 1)
+    assert ws(1, 0, 2, 16, 0) >= 256
+    assert ws(1, 10, 2, 48, 1) == 0  # unsupported Dh
+    assert ws(0, 10, 2, 16, 1) == 0
+    assert ws(1, 10, 2, 16, 7) == 0
+    ck = lib.esa_scan_ckpt_bytes
+    assert ck(2, 64, 3, 16) == 2 * 1 * 3 * 16 * 4
+    assert ck(2, 65, 3, 16) == 2 * 2 * 3 * 16 * 4
+    assert ck(2, 0, 3, 16) == 0
+
+
+# fake, 16-byte aligned, non-overlapping device addresses (never dereferenced)
+def addr(k):
+    return ctypes.c_void_p(0x100000000 + k * 0x10000000)
+
+
+def fwd(lib, B=2, T=100, H=2, Dh=16, dt=1, mode=1, a=1, v=2, q=3, e0=None, y=4, eT=5, ck=None,
+        ws=6, wsb=None):
+    def p(k):
+        if k is None:
+            return None
+        return k if isinstance(k, ctypes.c_void_p) else addr(k)
+
+    if wsb is None:
+        wsb = 0
+    return lib.esa_scan_fwd(B, T, H, Dh, dt, mode, p(a), p(v), p(q), p(e0), p(y), p(eT), p(ck),
+                            p(ws), wsb, None)
+
+
+def test_fwd_validation(lib):
+    assert fwd(lib, a=None) == INVALID
+    # T = 0 needs no sequence pointers; with no final state nothing is launched
+    assert fwd(lib, a=None, v=None, q=None, y=None, eT=None, T=0, ws=None) == OK
+    assert fwd(lib, y=None) == INVALID
+    assert fwd(lib, B=0) == INVALID
+    assert fwd(lib, T=-1) == INVALID
+    assert fwd(lib, dt=3) == INVALID
+    assert fwd(lib, mode=2) == INVALID
+    assert fwd(lib, Dh=48) == UNSUPPORTED
+    assert fwd(lib, Dh=256) == UNSUPPORTED
+    assert fwd(lib, B=1 << 40, T=1 << 40) == INVALID  # element count overflows int64
+    mis = ctypes.c_void_p(0x100000000 + 8)
+    assert fwd(lib, v=mis) == INVALID
+    assert fwd(lib, ws=None) == WORKSPACE
+    assert fwd(lib, wsb=100) == WORKSPACE
+    # y overlapping an input
+    assert fwd(lib, y=1) == INVALID
+    # final state overlapping the workspace
+    assert fwd(lib, eT=6, wsb=1000) == INVALID
+
+
+def test_bwd_validation(lib):
+    def bwd(**kw):
+        args = dict(B=2, T=100, H=2, Dh=64, dt=2, mode=0)
+        args.update({k: kw.pop(k) for k in list(kw) if k in args})
+        ptr = dict(a=1, v=2, q=3, e0=None, dy=4, dET=None, ck=None, da=5, dv=6, dq=7, de0=None,
+                   ws=8)
+        ptr.update(kw)
+        p = {k: (None if x is None else addr(x)) for k, x in ptr.items()}
+        return lib.esa_scan_bwd(args["B"], args["T"], args["H"], args["Dh"], args["dt"],
+                                args["mode"], p["a"], p["v"], p["q"], p["e0"], p["dy"], p["dET"],
+                                p["ck"], p["da"], p["dv"], p["dq"], p["de0"], p["ws"], 0, None)
+
+    assert bwd(dy=None) == INVALID
+    assert bwd(dq=None) == INVALID
+    assert bwd(Dh=8) == UNSUPPORTED
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(da=4) == INVALID  # gradient output overlaps dy
+    assert bwd(dv=5) == INVALID  # two outputs overlap
+
+
+def test_step_validation(lib):
+    def step(B=4, H=2, Dh=64, dt=1, mode=1, a=1, v=2, q=3, st=4, y=5):
+        p = [None if x is None else addr(x) for x in (a, v, q, st, y)]
+        return lib.esa_state_step(B, H, Dh, dt, mode, *p, None)
+
+    assert step(st=None) == INVALID
+    assert step(y=None) == INVALID
+    assert step(Dh=24) == UNSUPPORTED
+    assert step(y=2) == INVALID
+    assert step(st=1) == INVALID
+    assert step(mode=-1) == INVALID
+
+
+def test_workspace_init_validation(lib):
+    assert lib.esa_workspace_init(None, 256, None) == INVALID
+    assert lib.esa_workspace_init(ctypes.c_void_p(0x100000008), 256, None) == INVALID

@@ -1,0 +1,321 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle, element by element.
+
+Sizes are ones the oracle finishes in seconds while still spanning several tiles and a
+ragged tail; every dtype, mode and head size the library supports appears.  The five
+workloads (tests/../gated_linear_recurrence_chunked_amd/synth.py) also run at full size in
+the launch configuration the benchmark times, compared on whole sampled batch rows (every
+row is an independent problem the oracle solves exactly).
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_linear_recurrence_chunked_amd import binding, synth
+from helpers import TOL, assert_close, err, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+MODES = {"direct": 0, "controlled": 1}
+
+
+def seed_of(*parts) -> int:
+    """A seed that depends only on the case (not on Python's per-process string hashing)."""
+    return zlib.crc32(repr(parts).encode()) % 100000
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def inputs_cpu(B, T, H, Dh, dtype, seed, a_mean=0.0, a_std=1.5, dy=False):
+    shp = (B, T, H, Dh)
+    out = {
+        "a": synth.normal(shp, seed, a_mean, a_std, dtype),
+        "v": synth.normal(shp, seed + 1, 0.0, 1.0, dtype),
+        "q": synth.normal(shp, seed + 2, 0.0, 1.0, dtype),
+    }
+    if dy:
+        out["dy"] = synth.normal(shp, seed + 3, 0.0, 1.0, dtype)
+    return out
+
+
+def check_abort_clear():
+    for ws in binding._workspaces.values():
+        torch.cuda.synchronize()
+        assert int(ws[12:16].view(torch.int32).item()) == 0, "look-back wait timed out"
+
+
+# (B, T, H, Dh): single tile, ragged tails, many tiles, channel blocks that do not fill
+SHAPES = [
+    (1, 1, 1, 16),
+    (2, 63, 2, 16),
+    (1, 65, 1, 128),
+    (3, 129, 3, 32),
+    (2, 1000, 2, 64),
+    (1, 4097, 1, 64),
+    (5, 300, 1, 16),
+    (2, 777, 2, 128),
+    (1, 256, 2, 16),
+]
+DTYPE_MODE = [("f32", "direct"), ("f32", "controlled"), ("f16", "controlled"), ("f16", "direct"),
+              ("bf16", "direct"), ("bf16", "controlled")]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dt,mode", DTYPE_MODE)
+def test_fwd_parity(shape, dt, mode):
+    B, T, H, Dh = shape
+    dtype = DT[dt]
+    say(f"fwd {shape} {dt} {mode}")
+    x = inputs_cpu(B, T, H, Dh, dtype, seed=seed_of(shape, dt, mode))
+    e0 = synth.random_state(B, H, Dh, seed=7) if T % 2 else None
+    g = {k: t.to(DEV) for k, t in x.items()}
+    y, eT, ck = binding.scan_fwd(g["a"], g["v"], g["q"], None if e0 is None else e0.to(DEV),
+                                 mode=mode, return_ckpt=True)
+    torch.cuda.synchronize()
+    ry, reT, rE = oracle.scan_fwd(x["a"], x["v"], x["q"], e0, mode=MODES[mode], states=True,
+                                  threads=8)
+    assert_close("y", y, ry, dtype)
+    assert_close("final_state", eT, reT, dtype)
+    nck = -(-T // 64)
+    ckv = ck[: B * nck * H * Dh].view(B, nck, H, Dh)
+    idx = [min(T, 64 * (k + 1)) - 1 for k in range(nck)]
+    assert_close("ckpt", ckv, rE[:, idx], dtype)
+    check_abort_clear()
+
+
+@pytest.mark.parametrize("shape", SHAPES[1:], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dt,mode", DTYPE_MODE)
+def test_bwd_parity(shape, dt, mode):
+    B, T, H, Dh = shape
+    dtype = DT[dt]
+    say(f"bwd {shape} {dt} {mode}")
+    x = inputs_cpu(B, T, H, Dh, dtype, seed=seed_of(shape, dt, mode, 1), a_mean=0.5,
+                   dy=True)
+    e0 = synth.random_state(B, H, Dh, seed=8) if T % 2 else None
+    dET = synth.random_state(B, H, Dh, seed=9) if T % 3 else None
+    g = {k: t.to(DEV) for k, t in x.items()}
+    ge0 = None if e0 is None else e0.to(DEV)
+    gdET = None if dET is None else dET.to(DEV)
+    _, _, ck = binding.scan_fwd(g["a"], g["v"], g["q"], ge0, mode=mode, return_ckpt=True)
+    da, dv, dq, de0 = binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], ge0, gdET, ckpt=ck,
+                                       mode=mode)
+    # the same without a checkpoint (the library recomputes it)
+    da2, dv2, dq2, de02 = binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], ge0, gdET, ckpt=None,
+                                           mode=mode)
+    torch.cuda.synchronize()
+    r = oracle.scan_bwd(x["a"], x["v"], x["q"], x["dy"], e0, dET, mode=MODES[mode], threads=8)
+    for name, got, got2, ref in zip(("d_logit", "d_value", "d_query", "d_init"),
+                                    (da, dv, dq, de0), (da2, dv2, dq2, de02), r):
+        assert_close(name, got, ref, dtype)
+        assert_close(name + " (no ckpt)", got2, ref, dtype)
+    check_abort_clear()
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("Dh", [16, 32, 64, 128])
+@pytest.mark.parametrize("mode", ["direct", "controlled"])
+def test_step_parity(dt, Dh, mode):
+    dtype = DT[dt]
+    B, H = 7, 3
+    say(f"step B={B} H={H} Dh={Dh} {dt} {mode}")
+    x = inputs_cpu(B, 1, H, Dh, dtype, seed=Dh * 31 + len(dt))
+    st0 = synth.random_state(B, H, Dh, seed=11)
+    st = st0.to(DEV)
+    y = binding.state_step(x["a"][:, 0].contiguous().to(DEV), x["v"][:, 0].contiguous().to(DEV),
+                           x["q"][:, 0].contiguous().to(DEV), st, mode=mode)
+    torch.cuda.synchronize()
+    ry, rst = oracle.state_step(x["a"][:, 0], x["v"][:, 0], x["q"][:, 0], st0, mode=MODES[mode])
+    assert_close("y", y, ry, dtype)
+    assert_close("state", st, rst, dtype)
+
+
+def test_empty_sequence():
+    say("empty sequence")
+    B, H, Dh = 2, 2, 32
+    z = torch.zeros((B, 0, H, Dh), dtype=torch.float16, device=DEV)
+    e0 = synth.random_state(B, H, Dh, seed=3).to(DEV)
+    y, eT = binding.scan_fwd(z, z.clone(), z.clone(), e0, mode="controlled")
+    assert y.shape == z.shape
+    torch.testing.assert_close(eT, e0, rtol=0, atol=0)
+    y, eT = binding.scan_fwd(z, z.clone(), z.clone(), None, mode="controlled")
+    torch.testing.assert_close(eT, torch.zeros_like(eT), rtol=0, atol=0)
+    dET = synth.random_state(B, H, Dh, seed=4).to(DEV)
+    _, _, _, dI = binding.scan_bwd(z, z.clone(), z.clone(), z.clone(), e0, dET, mode="controlled")
+    torch.testing.assert_close(dI, dET, rtol=0, atol=0)
+
+
+def test_in_place_final_state():
+    say("in-place final state")
+    B, T, H, Dh = 2, 700, 2, 64
+    x = inputs_cpu(B, T, H, Dh, torch.float16, seed=123)
+    e0 = synth.random_state(B, H, Dh, seed=5)
+    g = {k: t.to(DEV) for k, t in x.items()}
+    st = e0.to(DEV)
+    y, eT = binding.scan_fwd(g["a"], g["v"], g["q"], st, mode="controlled", final_state=st)
+    torch.cuda.synchronize()
+    ry, reT = oracle.scan_fwd(x["a"], x["v"], x["q"], e0, mode=1)
+    assert eT.data_ptr() == st.data_ptr()
+    assert_close("y", y, ry, torch.float16)
+    assert_close("state", st, reT, torch.float16)
+
+
+def test_saturated_gates_reach_special_cases():
+    """a = +100 gives A = 1 exactly (a prefix sum over t); a = -100 gives A ~ 0 (E = v)."""
+    say("saturated gates")
+    B, T, H, Dh = 2, 256, 2, 16
+    v = synth.normal((B, T, H, Dh), 31, 0, 1, torch.float32)
+    q = synth.normal((B, T, H, Dh), 32, 0, 1, torch.float32)
+    for val, ref_E in ((100.0, np.cumsum(f64(v), axis=1)), (-100.0, f64(v))):
+        a = torch.full_like(v, val)
+        y, eT, ck = binding.scan_fwd(a.to(DEV), v.to(DEV), q.to(DEV), mode="direct",
+                                     return_ckpt=True)
+        torch.cuda.synchronize()
+        assert err(eT, ref_E[:, -1]) <= 1e-5
+        ckv = ck.view(B, T // 64, H, Dh)
+        assert err(ckv, ref_E[:, 63::64]) <= 1e-5
+        ry, _ = oracle.scan_fwd(a, v, q, mode=0)
+        assert_close("y", y, ry, torch.float32)
+
+
+def test_workspace_reuse_across_shapes():
+    """One cached workspace serves problems of different shapes in turn (the epoch tags keep
+    stale look-back words of earlier calls from matching)."""
+    say("workspace reuse")
+    cases = [(2, 3000, 2, 64, torch.float16), (1, 500, 4, 32, torch.bfloat16),
+             (2, 3000, 2, 64, torch.float16), (3, 129, 1, 128, torch.float32)]
+    for B, T, H, Dh, dtype in cases + cases:
+        x = inputs_cpu(B, T, H, Dh, dtype, seed=B * 1000 + T)
+        g = {k: t.to(DEV) for k, t in x.items()}
+        y, eT = binding.scan_fwd(g["a"], g["v"], g["q"], mode="controlled")
+        torch.cuda.synchronize()
+        ry, reT = oracle.scan_fwd(x["a"], x["v"], x["q"], mode=1, threads=8)
+        assert_close("y", y, ry, dtype)
+        assert_close("eT", eT, reT, dtype)
+    check_abort_clear()
+
+
+def test_resume_equals_unsplit():
+    """scan(T1) then scan(T2, E0 = E_T1) equals scan(T1 + T2), within tolerance."""
+    say("resume")
+    B, T1, T2, H, Dh = 2, 1000, 600, 2, 64
+    x = inputs_cpu(B, T1 + T2, H, Dh, torch.float16, seed=77)
+    g = {k: t.to(DEV) for k, t in x.items()}
+    y, eT = binding.scan_fwd(g["a"], g["v"], g["q"], mode="controlled")
+    y1, e1 = binding.scan_fwd(g["a"][:, :T1], g["v"][:, :T1], g["q"][:, :T1], mode="controlled")
+    y2, e2 = binding.scan_fwd(g["a"][:, T1:], g["v"][:, T1:], g["q"][:, T1:], e1, mode="controlled")
+    torch.cuda.synchronize()
+    assert err(torch.cat([y1, y2], 1), y) <= 5e-3
+    assert err(e2, eT) <= 1e-5
+
+
+# ---------------------------------------------------------------------------------------
+# The five workloads at full size, compared on sampled batch rows.
+# ---------------------------------------------------------------------------------------
+def gpu_inputs(wl, T=None, dy=False):
+    return synth.make_inputs(wl, device=DEV, T=T, with_dy=dy)
+
+
+def rows(t, idx):
+    return t[idx].to("cpu")
+
+
+def test_workload_small_fwd_f32():
+    wl = synth.WORKLOADS["small_fwd_f32"]
+    say(f"workload {wl.name}")
+    g = gpu_inputs(wl)
+    y, eT = binding.scan_fwd(g["a"], g["v"], g["q"], mode=wl.mode)
+    torch.cuda.synchronize()
+    ry, reT = oracle.scan_fwd(g["a"].cpu(), g["v"].cpu(), g["q"].cpu(), mode=MODES[wl.mode])
+    assert_close("y", y, ry, torch.float32)
+    assert_close("eT", eT, reT, torch.float32)
+
+
+def test_workload_layer_fwd_f16():
+    wl = synth.WORKLOADS["layer_fwd_f16"]
+    say(f"workload {wl.name}")
+    g = gpu_inputs(wl)
+    y, eT = binding.scan_fwd(g["a"], g["v"], g["q"], mode=wl.mode)
+    torch.cuda.synchronize()
+    ry, reT = oracle.scan_fwd(g["a"].cpu(), g["v"].cpu(), g["q"].cpu(), mode=MODES[wl.mode],
+                              threads=8)
+    assert_close("y", y, ry, torch.float16)
+    assert_close("eT", eT, reT, torch.float16)
+
+
+def _fwd_bwd_rows(wl, sample):
+    dtype = DT[wl.dtype]
+    g = gpu_inputs(wl, dy=True)
+    y, eT, ck = binding.scan_fwd(g["a"], g["v"], g["q"], mode=wl.mode, return_ckpt=True)
+    da, dv, dq, de0 = binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], ckpt=ck, mode=wl.mode)
+    torch.cuda.synchronize()
+    check_abort_clear()
+    for b in sample:
+        say(f"  row {b}")
+        xa, xv, xq, xd = (rows(g[k], [b]) for k in ("a", "v", "q", "dy"))
+        ry, reT = oracle.scan_fwd(xa, xv, xq, mode=MODES[wl.mode])
+        assert_close(f"y[{b}]", rows(y, [b]), ry, dtype)
+        assert_close(f"eT[{b}]", rows(eT, [b]), reT, dtype)
+        r = oracle.scan_bwd(xa, xv, xq, xd, mode=MODES[wl.mode])
+        for name, got, ref in zip(("d_logit", "d_value", "d_query", "d_init"),
+                                  (da, dv, dq, de0), r):
+            assert_close(f"{name}[{b}]", rows(got, [b]), ref, dtype)
+    del g, y, eT, ck, da, dv, dq, de0
+    torch.cuda.empty_cache()
+
+
+def test_workload_train8k_bf16():
+    wl = synth.WORKLOADS["train8k_bf16"]
+    say(f"workload {wl.name}")
+    _fwd_bwd_rows(wl, [0, 9, 15])
+
+
+def test_workload_long64k_f16():
+    wl = synth.WORKLOADS["long64k_f16"]
+    say(f"workload {wl.name}")
+    _fwd_bwd_rows(wl, [0, 63])
+
+
+def test_workload_decode_f16():
+    """Prefill at every prompt length, then decode steps, against the oracle on sampled rows;
+    prefill + steps also equals one longer scan of the same inputs."""
+    wl = synth.WORKLOADS["decode_f16"]
+    dtype = DT[wl.dtype]
+    n_steps = 8
+    sample = [0, 131, 255]
+    for T in wl.prompts:
+        say(f"workload {wl.name} prompt {T}")
+        g = gpu_inputs(wl, T=T)
+        y, st = binding.scan_fwd(g["a"], g["v"], g["q"], mode=wl.mode)
+        torch.cuda.synchronize()
+        ry, rst = oracle.scan_fwd(rows(g["a"], sample), rows(g["v"], sample), rows(g["q"], sample),
+                                  mode=1, threads=3)
+        assert_close("prefill y", rows(y, sample), ry, dtype)
+        assert_close("prefill state", rows(st, sample), rst, dtype)
+        if T != wl.prompts[0]:
+            continue
+        # decode steps, chained from the prefill state
+        seq_a, seq_v, seq_q, ys = [g["a"]], [g["v"]], [g["q"]], []
+        for k in range(n_steps):
+            s = synth.decode_step_inputs(wl, k, device=DEV)
+            ys.append(binding.state_step(s["a"], s["v"], s["q"], st, mode=wl.mode))
+            seq_a.append(s["a"][:, None])
+            seq_v.append(s["v"][:, None])
+            seq_q.append(s["q"][:, None])
+            torch.cuda.synchronize()
+            ryk, rst = oracle.state_step(rows(s["a"], sample), rows(s["v"], sample),
+                                         rows(s["q"], sample), rst, mode=1)
+            assert_close(f"step {k} y", rows(ys[-1], sample), ryk, dtype)
+            assert_close(f"step {k} state", rows(st, sample), rst, dtype)
+        # prefill + steps == one scan over prompt + generated tokens
+        A, V, Q = (torch.cat(s, 1).contiguous() for s in (seq_a, seq_v, seq_q))
+        yl, stl = binding.scan_fwd(A, V, Q, mode=wl.mode)
+        torch.cuda.synchronize()
+        assert err(st, stl) <= 1e-5
+        assert err(torch.stack(ys, 1), yl[:, T:]) <= TOL[dtype]
