@@ -1,0 +1,277 @@
+"""Benchmark of the ESA gated linear recurrence on one MI355X.
+
+Headline: fwd + bwd scan tokens/s on the 64K-context workload (B=64, T=65536, H=8, Dh=64,
+fp16 storage, controlled mode), with the dominant kernel's fraction of the HBM roofline,
+plus decode steps/s on the generation workload (B=256, H=8, Dh=64, fp16; prefill at prompt
+lengths 512 / 1K / 4K / 8K, then 1024 one-token steps).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = esa_scan_fwd (with checkpoint) + esa_scan_bwd over the whole batch, inputs
+resident in HBM.  Timing uses HIP events on the stream the kernels run on, around every
+launch, so the per-kernel averages come from the same timed region as the total.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="0 = min(16, cpu count)")
+    ap.add_argument("--only", choices=["train", "decode", "all", "copy"], default="all",
+                    help="copy: a plain 4 GiB device copy, the reference for HBM counters")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def bench_train(args, torch, binding, synth):
+    wl = synth.WORKLOADS["long64k_f16"]
+    B, T, H, Dh = wl.B, wl.T, wl.H, wl.Dh
+    log(f"[bench] {wl.name}: generating inputs B={B} T={T} H={H} Dh={Dh} {wl.dtype}")
+    g = synth.make_inputs(wl, device="cuda:0", with_dy=True)
+    torch.cuda.synchronize()
+    nelem = B * T * H * Dh
+    sb = g["a"].element_size()
+    ck_bytes = binding.ckpt_bytes(B, T, H, Dh)
+    st_bytes = B * H * Dh * 4
+    # algorithmic bytes per launch: what the method itself must read and write
+    fwd_bytes = nelem * 4 * sb + ck_bytes + st_bytes  # a, v, q in; y out; ckpt + E_T out
+    bwd_bytes = nelem * 7 * sb + ck_bytes  # a, v, q, dy in; da, dv, dq out; ckpt in
+
+    y = torch.empty_like(g["a"])
+    eT = torch.empty((B, H, Dh), dtype=torch.float32, device="cuda:0")
+
+    def step():
+        _, _, ck = binding.scan_fwd(g["a"], g["v"], g["q"], mode=wl.mode, return_ckpt=True,
+                                    final_state=eT, y=y)
+        return ck
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        ck = step()
+        binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], ckpt=ck, mode=wl.mode)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record()
+        ck = step()
+        ev[k][1].record()
+        binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], ckpt=ck, mode=wl.mode)
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    total_ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
+    out = {
+        "B": B, "T": T, "H": H, "Dh": Dh, "nelem": nelem,
+        "ms_per_step": total_ms, "wall_ms_per_step": wall * 1e3 / args.steps,
+        "fwd_ms": sum(fwd_ms) / len(fwd_ms), "bwd_ms": sum(bwd_ms) / len(bwd_ms),
+        "fwd_bytes": fwd_bytes, "bwd_bytes": bwd_bytes, "tokens": B * T,
+    }
+    out["tokens_per_s"] = B * T / (total_ms * 1e-3)
+    out["fwd_gbs"] = fwd_bytes / (out["fwd_ms"] * 1e-3) / 1e9
+    out["bwd_gbs"] = bwd_bytes / (out["bwd_ms"] * 1e-3) / 1e9
+    out["fwd_tokens_per_s"] = B * T / (out["fwd_ms"] * 1e-3)
+    if not args.no_cpu_baseline:  # distinct batch rows for the oracle's timed sample
+        out["inputs"] = {k: g[k][: args.cpu_threads].cpu() for k in ("a", "v", "q", "dy")}
+    del g, y, eT
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_decode(args, torch, binding, synth):
+    wl = synth.WORKLOADS["decode_f16"]
+    B, H, Dh = wl.B, wl.H, wl.Dh
+    res = {"B": B, "H": H, "Dh": Dh, "prefill": {}}
+    n = args.decode_steps
+    log(f"[bench] decode: {n} step inputs")
+    steps = [synth.decode_step_inputs(wl, k, device="cuda:0") for k in range(n)]
+    torch.cuda.synchronize()
+    for T in wl.prompts:
+        g = synth.make_inputs(wl, device="cuda:0", T=T)
+        y, st = binding.scan_fwd(g["a"], g["v"], g["q"], mode=wl.mode)  # warm
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            y, st = binding.scan_fwd(g["a"], g["v"], g["q"], mode=wl.mode, y=y)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = B * T * H * Dh * 4 * 2 + B * H * Dh * 4
+        # decode: 1024 steps chained from the prefill state
+        ys = torch.empty((B, H, Dh), dtype=torch.float16, device="cuda:0")
+        for s in steps[:8]:
+            binding.state_step(s["a"], s["v"], s["q"], st.clone(), mode=wl.mode, y=ys)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record()
+        for s in steps:
+            binding.state_step(s["a"], s["v"], s["q"], st, mode=wl.mode, y=ys)
+        d1.record()
+        torch.cuda.synchronize()
+        dms = d0.elapsed_time(d1)
+        res["prefill"][str(T)] = {
+            "ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "decode_us_per_step": dms * 1e3 / n, "decode_steps_per_s": n / (dms * 1e-3),
+        }
+        del g, y
+        torch.cuda.empty_cache()
+    sps = [v["decode_steps_per_s"] for v in res["prefill"].values()]
+    res["decode_steps_per_s"] = sum(sps) / len(sps)
+    # the same chain of steps captured once into a HIP graph and replayed (no per-launch
+    # host work); the step kernel records no memset node
+    st_g = st.clone()
+    ys_g = torch.empty((B, H, Dh), dtype=torch.float16, device="cuda:0")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for s in steps[:4]:
+            binding.state_step(s["a"], s["v"], s["q"], st_g.clone(), mode=wl.mode, y=ys_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in steps:
+            binding.state_step(s["a"], s["v"], s["q"], st_g, mode=wl.mode, y=ys_g)
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    g0.record()
+    for _ in range(reps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    gms = g0.elapsed_time(g1) / reps
+    res["decode_graph_us_per_step"] = gms * 1e3 / n
+    res["decode_graph_steps_per_s"] = n / (gms * 1e-3)
+    del graph
+    res["decode_tokens_per_s"] = res["decode_steps_per_s"] * B
+    res["decode_step_bytes"] = B * H * Dh * (4 * 2 + 2 * 4)
+    return res
+
+
+def cpu_baseline(args, train):
+    """The oracle, as it stands, on a bounded sample of the 64K workload: whole batch rows
+    (every row is an independent problem), one row per thread, fwd + bwd."""
+    import numpy as np
+
+    import oracle
+
+    threads = args.cpu_threads
+    x = train["inputs"]
+    # the sample: the first `threads` batch rows, so each thread runs one full row
+    a, v, q, dy = (oracle._f64(x[k]) for k in ("a", "v", "q", "dy"))
+    log(f"[bench] cpu baseline: oracle fwd+bwd on {threads} rows of T={a.shape[1]} "
+        f"with {threads} threads")
+    t0 = time.perf_counter()
+    oracle.scan_fwd(a, v, q, mode=1, threads=threads)
+    oracle.scan_bwd(a, v, q, dy, mode=1, threads=threads)
+    sec = time.perf_counter() - t0
+    tokens = a.shape[0] * a.shape[1]
+    return {"value": tokens / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": sec,
+            "sample": f"{a.shape[0]} batch rows x T={a.shape[1]} (H=8, Dh=64, fp64, controlled) "
+                      f"fwd+bwd, one row per thread"}
+
+
+def bench_copy(args, torch):
+    """A plain device-to-device copy of 4 GiB: reads and writes exactly 4 GiB each, the
+    reference that scales the HBM traffic counters (FETCH_SIZE, WRITE_SIZE)."""
+    n = 1 << 32
+    x = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(args.warmup + args.steps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    return {"copy_bytes": n, "launches": args.warmup + args.steps}
+
+
+def main():
+    args = parse()
+    args.cpu_threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU figures "
+                                   "are not part of this build (see the sharding note in the "
+                                   "design notes)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    from gated_linear_recurrence_chunked_amd import binding, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load_library()
+    result = {"metric": "scan fwd+bwd tokens/s and % of HBM peak at 64K ctx; decode steps/s",
+              "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+              "data": "synthetic (seeded N(mu, sigma) draws shaped like the pages' workloads)"}
+    train = None
+    if args.only == "copy":
+        result["copy"] = bench_copy(args, torch)
+        print(json.dumps(result), flush=True)
+        return
+    if args.only in ("train", "all"):
+        train = bench_train(args, torch, binding, synth)
+        result["value"] = train["tokens_per_s"]
+        result["ms_per_step"] = train["ms_per_step"]
+        result["config"] = {"workload": "long64k_f16: 64K-context fwd+bwd scan", "B": train["B"],
+                            "T": train["T"], "H": train["H"], "Dh": train["Dh"],
+                            "mode": "controlled", "storage": "f16", "accumulate": "f32",
+                            "global_batch": train["B"], "seq_len": train["T"],
+                            "parallelism": "single GPU"}
+        dom = "bwd" if train["bwd_ms"] >= train["fwd_ms"] else "fwd"
+        ach = train[f"{dom}_gbs"]
+        result["roofline"] = {"kernel": f"esa {dom}_kernel (f16, controlled, Dh=64)",
+                              "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                              "traffic": None,
+                              "algorithmic_bytes_per_launch": train[f"{dom}_bytes"],
+                              "avg_launch_ms": round(train[f"{dom}_ms"], 4)}
+        result["kernels"] = {
+            "fwd": {"ms": round(train["fwd_ms"], 4), "GB_s": round(train["fwd_gbs"], 1),
+                    "frac_hbm": round(train["fwd_gbs"] / HBM_PEAK_GBS, 4),
+                    "tokens_per_s": train["fwd_tokens_per_s"],
+                    "algorithmic_bytes": train["fwd_bytes"]},
+            "bwd": {"ms": round(train["bwd_ms"], 4), "GB_s": round(train["bwd_gbs"], 1),
+                    "frac_hbm": round(train["bwd_gbs"] / HBM_PEAK_GBS, 4),
+                    "algorithmic_bytes": train["bwd_bytes"]},
+        }
+    if args.only in ("decode", "all"):
+        dec = bench_decode(args, torch, binding, synth)
+        result["decode"] = dec
+    if train is not None and not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, train)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

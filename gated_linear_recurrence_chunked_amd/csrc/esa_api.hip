@@ -3,6 +3,10 @@
 // changes nothing on the device.  The library allocates nothing and never synchronises.
 #include <stdint.h>
 #include <string.h>
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
 
 #include "esa.h"
 #include "esa_common.hpp"
@@ -85,7 +89,7 @@ int layout_of(const Problem& pr, Layout* L) {
     const int64_t nTB = pr.T > 0 ? cdiv(pr.T, ts.TTb) : 0;
     const int64_t nTM = nTF > nTB ? nTF : nTB;
     int64_t nwg, words, xbytes, ckbytes;
-    if (!mul64(nCB, nTM, &nwg) || nwg > (int64_t)UINT32_MAX || nCB > (int64_t)UINT32_MAX)
+    if (!mul64(nCB, nTM, &nwg) || nwg > (int64_t)INT32_MAX)
         return ESA_ERR_UNSUPPORTED;
     if (!mul64(nTM, pr.nLanes, &words) || !mul64(words, 8, &xbytes)) return ESA_ERR_UNSUPPORTED;
     L->nCB = (uint32_t)nCB;
@@ -165,6 +169,14 @@ hipError_t step_dh(int64_t Dh, const StepParams& p, hipStream_t s) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ESA_OK : ESA_ERR_HIP; }
+
+// Epochs tag the look-back words of one scan kernel launch.  The counter is process-wide and
+// only ever increments, so a workspace never sees the same epoch twice within 2^30 launches;
+// its start is drawn from the clock and the process id.
+std::atomic<uint32_t> g_epoch{(uint32_t)(std::chrono::steady_clock::now().time_since_epoch().count() ^
+                                         ((uint64_t)getpid() << 16))};
+
+uint32_t next_epoch() { return g_epoch.fetch_add(1, std::memory_order_relaxed) & 0x3fffffffu; }
 
 }  // namespace
 
@@ -251,7 +263,7 @@ int esa_scan_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mod
     p.nck = L.nck;
     p.nCB = L.nCB;
     p.nTiles = L.nTilesF;
-    p.nWG = L.nCB * L.nTilesF;
+    p.epoch = next_epoch();
     return hip_status(ESA_DISPATCH(fwd, dtype, mode, Dh, p, s));
 }
 
@@ -308,7 +320,7 @@ int esa_scan_bwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mod
         f.nck = L.nck;
         f.nCB = L.nCB;
         f.nTiles = L.nTilesF;
-        f.nWG = L.nCB * L.nTilesF;
+        f.epoch = next_epoch();
         rc = hip_status(ESA_DISPATCH(fwd, dtype, mode, Dh, f, s));
         if (rc != ESA_OK) return rc;
         ck = f.ckpt;
@@ -334,7 +346,7 @@ int esa_scan_bwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mod
     p.nck = L.nck;
     p.nCB = L.nCB;
     p.nTiles = L.nTilesB;
-    p.nWG = L.nCB * L.nTilesB;
+    p.epoch = next_epoch();
     return hip_status(ESA_DISPATCH(bwd, dtype, mode, Dh, p, s));
 }
 

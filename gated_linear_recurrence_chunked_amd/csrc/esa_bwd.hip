@@ -10,7 +10,7 @@
 //   direct    d_logit = dE_t E_{t-1} s (1 - s),          d_value = dE_t
 //   controlled d_logit = dE_t (E_{t-1} - v_t) s (1 - s), d_value = dE_t (1 - s)
 // The reverse recurrence lam_t = s_t (gE_t + lam_{t+1}) is the same affine pair scan as
-// the forward, run from the end of the sequence: tiles are ticketed from the last one and
+// the forward, run from the end of the sequence: workgroup IDs number tiles from the last one and
 // look back toward later tiles.
 //
 // A tile first re-runs the forward inside itself from the checkpointed state at its start
@@ -30,13 +30,12 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     __shared__ float sP[S][CB];
     __shared__ float sE[S][CB];
 
-    uint32_t ticket, epoch;
-    take_ticket(p.hdr, ticket, epoch);
-    const uint32_t rtile = ticket / p.nCB;
-    const uint32_t cb = ticket - rtile * p.nCB;
-    const uint32_t tile = p.nTiles - 1 - rtile;
-    const uint32_t tagAgg = make_tag(epoch, kTagAgg);
-    const uint32_t tagInc = make_tag(epoch, kTagInc);
+    const uint32_t wg = blockIdx.x;
+    const uint32_t rtile = wg / p.nCB;
+    const uint32_t cb = wg - rtile * p.nCB;
+    const uint32_t tile = p.nTiles - 1 - rtile;  // the backward walks tiles from the end
+    const uint32_t tagAgg = make_tag(p.epoch, kTagAgg);
+    const uint32_t tagInc = make_tag(p.epoch, kTagInc);
 
     const int tid = threadIdx.x;
     const int j = tid % NCL;
@@ -241,14 +240,12 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
             st16(p.dv, base + i * p.C, ES, pack<T>(dvv));
         }
     }
-
-    if (tid == 0) finish_workgroup(p.hdr, p.nWG, epoch);
 }
 
 template <typename T, int MODE, int DH>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
     using C = BwdCfg<T, DH>;
-    hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT>), dim3(p.nWG), dim3(C::NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT>), dim3(p.nCB * p.nTiles), dim3(C::NT), 0, s, p);
     return hipGetLastError();
 }
 

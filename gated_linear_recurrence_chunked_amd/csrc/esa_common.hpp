@@ -16,13 +16,20 @@
 //   level 3  tiles of one channel block are chained by a decoupled look-back: a tile
 //            publishes its aggregate pair, then walks back over earlier tiles' published
 //            pairs until it meets an inclusive value, then publishes its own inclusive
-//            value.  Workgroups take tiles in ticket order (an atomic counter), so a tile
-//            only ever waits on tiles that are already running.
+//            value.
+//
+// Tile order.  Workgroup IDs are tile-major (id = tile * nCB + channel block; the backward
+// numbers tiles from the end), so a tile only ever waits on tiles with smaller IDs.  The
+// hardware starts the workgroups of one dispatch in increasing ID order on each XCD, so the
+// lowest unfinished workgroup is always resident and everything it waits on has finished:
+// the chain always makes progress, with no atomic counter per workgroup (a single-address
+// device atomic serialises at tens of ns each, which at 2^18 tiles would cost milliseconds).
+// Every wait is also bounded (see look_back), so even a broken chain ends.
 //
 // Look-back words are 64-bit (tag, fp32 value) pairs written and read with single-copy
 // atomic 64-bit accesses at agent scope, so no fence is needed between a value and its
-// flag.  The tag carries the call's epoch, so stale words from earlier calls never match
-// and the flag array needs no clearing between calls.
+// flag.  The tag carries a per-call epoch chosen by the host, so stale words from earlier
+// calls never match and the flag array needs no clearing between calls.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -84,10 +91,8 @@ struct BwdCfg {
 
 // Workspace layout: [header 256 B][flag X words][flag Y words][internal checkpoint].
 struct WsHeader {
-    uint32_t ticket;  // next tile ticket of the running kernel (self-resetting)
-    uint32_t done;    // workgroups finished (self-resetting)
-    uint32_t epoch;   // incremented by the last workgroup of every scan kernel
-    uint32_t abort;   // sticky: set when a look-back wait timed out (results are NaN)
+    uint32_t reserved[3];
+    uint32_t abort;  // sticky: set when a look-back wait timed out (results are then NaN)
     uint32_t pad[60];
 };
 static_assert(sizeof(WsHeader) == 256, "header must be 256 bytes");
@@ -112,7 +117,7 @@ struct FwdParams {
     int64_t nck;     // ceil(T / 64)
     uint32_t nCB;
     uint32_t nTiles;
-    uint32_t nWG;
+    uint32_t epoch;  // tags of this call's look-back words
 };
 
 struct BwdParams {
@@ -136,7 +141,7 @@ struct BwdParams {
     int64_t nck;
     uint32_t nCB;
     uint32_t nTiles;
-    uint32_t nWG;
+    uint32_t epoch;
 };
 
 struct StepParams {
@@ -309,31 +314,6 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
             }
         }
         __builtin_amdgcn_s_sleep(1);
-    }
-}
-
-// Ticket and epoch of this workgroup; called by all threads (contains a barrier).
-__device__ __forceinline__ void take_ticket(uint32_t* hdr, uint32_t& ticket, uint32_t& epoch) {
-    __shared__ uint32_t sT, sE;
-    if (threadIdx.x == 0) {
-        sT = __hip_atomic_fetch_add(&hdr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sE = __hip_atomic_load(&hdr[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    ticket = sT;
-    epoch = sE;
-}
-
-// Called by one thread at the very end of every workgroup: the last one resets the ticket
-// and done counters and advances the epoch for the next call.
-__device__ __forceinline__ void finish_workgroup(uint32_t* hdr, uint32_t nWG, uint32_t epoch) {
-    const uint32_t d =
-        __hip_atomic_fetch_add(&hdr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d == nWG - 1) {
-        __hip_atomic_store(&hdr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&hdr[2], (epoch + 1u) & 0x3fffffffu, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -20,12 +20,11 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     __shared__ float sE[S][CB];
     __shared__ float sCarry[CB];
 
-    uint32_t ticket, epoch;
-    take_ticket(p.hdr, ticket, epoch);
-    const uint32_t tile = ticket / p.nCB;
-    const uint32_t cb = ticket - tile * p.nCB;
-    const uint32_t tagAgg = make_tag(epoch, kTagAgg);
-    const uint32_t tagInc = make_tag(epoch, kTagInc);
+    const uint32_t wg = blockIdx.x;
+    const uint32_t tile = wg / p.nCB;
+    const uint32_t cb = wg - tile * p.nCB;
+    const uint32_t tagAgg = make_tag(p.epoch, kTagAgg);
+    const uint32_t tagInc = make_tag(p.epoch, kTagInc);
     const bool readout = p.y != nullptr;
 
     const int tid = threadIdx.x;
@@ -156,14 +155,12 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
                 *reinterpret_cast<float4*>(dst + e) = make_float4(E[e], E[e + 1], E[e + 2], E[e + 3]);
         }
     }
-
-    if (tid == 0) finish_workgroup(p.hdr, p.nWG, epoch);
 }
 
 template <typename T, int MODE, int DH>
 hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
     using C = FwdCfg<T, DH>;
-    hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT>), dim3(p.nWG), dim3(C::NT), 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT>), dim3(p.nCB * p.nTiles), dim3(C::NT), 0, s, p);
     return hipGetLastError();
 }
 

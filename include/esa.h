@@ -24,8 +24,9 @@
  * never allocates, frees or synchronises; each call validates its arguments on the host,
  * enqueues its kernels on `stream` (a hipStream_t; NULL is the default stream) and
  * returns.  Errors that occur while the kernels run surface at the caller's next
- * synchronisation.  The library holds no global state and is reentrant, but calls that
- * share one workspace must not run concurrently (use one workspace per stream).
+ * synchronisation.  The library is reentrant; its only global state is a process-wide
+ * counter that tags each scan launch's look-back words.  Calls that share one workspace
+ * must not run concurrently (use one workspace per stream).
  *
  * Errors.  Every entry point returns an esa_status.  All argument checks run before any
  * HIP call, so an invalid call changes nothing on the device:
@@ -33,7 +34,7 @@
  *                        16-byte aligned, element count overflowing int64, or an output
  *                        that overlaps an input
  *   ESA_ERR_UNSUPPORTED  Dh not in {16, 32, 64, 128}, or a problem whose tile count
- *                        exceeds 2^32 - 1
+ *                        exceeds 2^31 - 1
  *   ESA_ERR_WORKSPACE    workspace NULL or smaller than esa_scan_workspace_bytes()
  *   ESA_ERR_HIP          a kernel launch was rejected by the HIP runtime
  */
@@ -84,7 +85,10 @@ size_t esa_scan_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dh, int
  * t = 64 k + 63 for each chunk k (the last chunk holds E_{T-1}).  Returns 0 on bad sizes. */
 size_t esa_scan_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t Dh);
 
-/* Zero-fills `bytes` of workspace on `stream` (a fill kernel, safe inside graph capture). */
+/* Zero-fills `bytes` of workspace on `stream` (a fill kernel, safe inside graph capture).
+ * Word 3 of the workspace (bytes 12..15) is a sticky abort flag: it becomes non-zero if a
+ * scan's cross-tile wait ever timed out (about a second), in which case that call's results
+ * are NaN.  This never happens in a correct run; re-initialising the workspace clears it. */
 int esa_workspace_init(void *workspace, size_t bytes, void *stream);
 
 /* Forward scan with fused gate and readout: prefill and training forward (page "Entangled
