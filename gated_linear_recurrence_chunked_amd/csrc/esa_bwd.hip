@@ -16,49 +16,87 @@
 // A tile first re-runs the forward inside itself from the checkpointed state at its start
 // (level 1 and 2 of the forward scan, no look-back needed), keeping per element only what
 // the reverse pass uses: s, gE, the gate-gradient factor w and, in controlled mode, 1 - s.
+// As in the forward, every load is issued branch-free at a clamped, valid address, and
+// tiles entirely inside the problem skip the per-element masking and address their loads
+// and stores through buffer resources with one 32-bit lane offset.
 #include "esa_common.hpp"
 
 namespace esa {
 
-template <typename T, int MODE, int DH, int L, int NT>
-__global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
+template <typename T, int MODE, int DH, int L, int NT, bool FULL>
+__device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint32_t cb, float* sFP,
+                                         float* sFE, float* sRP, float* sRE, float* sCarry) {
     using G = Geom<T, DH, L, NT>;
-    constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, S = G::S, HL = G::HL;
-    constexpr int TT = G::TT;
+    constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, HL = G::HL;
+    constexpr int TT = G::TT, SPW = G::SPW, NW = G::NW;
     constexpr int ES = sizeof(T);
-
-    __shared__ float sP[S][CB];
-    __shared__ float sE[S][CB];
-
-    const uint32_t wg = blockIdx.x;
-    const uint32_t rtile = wg / p.nCB;
-    const uint32_t cb = wg - rtile * p.nCB;
-    const uint32_t tile = p.nTiles - 1 - rtile;  // the backward walks tiles from the end
     const uint32_t tagAgg = make_tag(p.epoch, kTagAgg);
     const uint32_t tagInc = make_tag(p.epoch, kTagInc);
 
     const int tid = threadIdx.x;
     const int j = tid % NCL;
     const int slot = tid / NCL;
+    const int w = tid / kWave;
+    const int sw = (tid % kWave) / NCL;
     const int64_t lane0 = (int64_t)cb * CB + j * VEC;
-    const bool lane_ok = lane0 < p.nLanes;
+    const bool lane_ok = FULL || lane0 < p.nLanes;
     const int64_t b = lane_ok ? lane0 / p.C : 0;
     const int64_t c = lane_ok ? lane0 - b * p.C : 0;
     const int64_t t0 = (int64_t)tile * TT + (int64_t)slot * L;
     const int64_t base = (b * p.T + t0) * p.C + c;
 
+    // ---- issue every load of the thread's L steps, branch-free ----
     uint4 ra[L], rv[L], rq[L], rd[L];
+    // full tiles: buffer resources at the tile's first element, one lane offset, row offsets
+    const int64_t g0 = (int64_t)cb * CB;
+    const int64_t bw = g0 / p.C;
+    const int64_t row0 = ((bw * p.T + (int64_t)tile * TT) * p.C + (g0 - bw * p.C)) * ES;
+    const uint32_t voff = (uint32_t)(((int64_t)slot * L * p.C + j * VEC) * ES);
+    const int32_t rstride = (int32_t)(p.C * ES);
+    if constexpr (FULL) {
+        const auto rs_a = make_rsrc(static_cast<const char*>(p.a) + row0);
+        const auto rs_v = make_rsrc(static_cast<const char*>(p.v) + row0);
+        const auto rs_q = make_rsrc(static_cast<const char*>(p.q) + row0);
+        const auto rs_d = make_rsrc(static_cast<const char*>(p.dy) + row0);
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-        ra[i] = make_uint4(0, 0, 0, 0);
-        rv[i] = make_uint4(0, 0, 0, 0);
-        rq[i] = make_uint4(0, 0, 0, 0);
-        rd[i] = make_uint4(0, 0, 0, 0);
-        if (lane_ok && t0 + i < p.T) {
-            ra[i] = ld16(p.a, base + i * p.C, ES);
-            rv[i] = ld16(p.v, base + i * p.C, ES);
-            rq[i] = ld16(p.q, base + i * p.C, ES);
-            rd[i] = ld16(p.dy, base + i * p.C, ES);
+        for (int i = 0; i < L; ++i) {
+            ra[i] = ldbuf(rs_a, voff, i * rstride);
+            rv[i] = ldbuf(rs_v, voff, i * rstride);
+            rq[i] = ldbuf(rs_q, voff, i * rstride);
+            rd[i] = ldbuf(rs_d, voff, i * rstride);
+        }
+    } else {
+        // ragged tile: rows past the end and lanes past the batch load a clamped, valid
+        // address and are masked below
+        const int64_t lc = lane_ok ? lane0 : 0;
+        const int64_t bc = lc / p.C, cc = lc - bc * p.C;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const int64_t t = t0 + i < p.T ? t0 + i : p.T - 1;
+            const int64_t off = (bc * p.T + t) * p.C + cc;
+            ra[i] = ld16(p.a, off, ES);
+            rv[i] = ld16(p.v, off, ES);
+            rq[i] = ld16(p.q, off, ES);
+            rd[i] = ld16(p.dy, off, ES);
+        }
+    }
+    // state entering the tile: the initial state, or the forward's checkpoint at the end of
+    // the previous 64-step chunk (masked lanes read a valid lane's value, then stay masked)
+    float cin[VEC];
+    {
+        const int64_t lc = lane_ok ? lane0 : 0;
+        const int64_t bc = lc / p.C, cc = lc - bc * p.C;
+        const float* src =
+            tile == 0 ? (p.e0 ? p.e0 + lc : nullptr)
+                      : p.ckpt + (bc * p.nck + (int64_t)tile * (TT / kCkptChunk) - 1) * p.C + cc;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+            float4 x = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (src) x = *reinterpret_cast<const float4*>(src + e);
+            cin[e] = x.x;
+            cin[e + 1] = x.y;
+            cin[e + 2] = x.z;
+            cin[e + 3] = x.w;
         }
     }
 
@@ -73,7 +111,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-        const bool ok = lane_ok && t0 + i < p.T;
+        const bool ok = FULL || (lane_ok && t0 + i < p.T);
         float av[VEC];
         unpack<T>(ra[i], av);
         unpack<T>(rv[i], V_[i]);
@@ -91,46 +129,45 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         }
     }
 
-    // ---- forward prefix within the tile, from the checkpointed state at its start ----
+    // ---- state entering this thread's steps: the checkpoint at the tile start, carried
+    //      through the earlier slots of the tile (two-level scan, no look-back needed) ----
+    wave_scan_fwd<NCL, SPW, VEC>(P, E, sw);
+    float XP[VEC], XE[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-        sP[slot][j * VEC + e] = P[e];
-        sE[slot][j * VEC + e] = E[e];
-    }
-    __syncthreads();
-    if (tid < kWave) {
-#pragma unroll
-        for (int k = 0; k < G::CPL; ++k) {
-            const int ch = tid + k * kWave;
-            const int64_t gl = (int64_t)cb * CB + ch;
-            float cin = 0.0f;
-            if (gl < p.nLanes) {
-                if (tile == 0) {
-                    cin = p.e0 ? p.e0[gl] : 0.0f;
-                } else {
-                    const int64_t gb = gl / p.C, gc = gl - gb * p.C;
-                    const int64_t ck = (int64_t)tile * (TT / kCkptChunk) - 1;
-                    cin = p.ckpt[(gb * p.nck + ck) * p.C + gc];
-                }
-            }
-            float te = cin;
-#pragma unroll 8
-            for (int s = 0; s < S; ++s) {
-                const float ps = sP[s][ch], es = sE[s][ch];
-                sE[s][ch] = te;  // state entering slot s
-                te = ps * te + es;
-            }
+        XP[e] = __shfl_up(P[e], NCL, kWave);
+        XE[e] = __shfl_up(E[e], NCL, kWave);
+        if (sw == 0) {
+            XP[e] = 1.0f;
+            XE[e] = 0.0f;
+        }
+        if (sw == SPW - 1) {
+            sFP[w * CB + j * VEC + e] = P[e];
+            sFE[w * CB + j * VEC + e] = E[e];
         }
     }
     __syncthreads();
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        float wp = 1.0f, we = 0.0f;
+#pragma unroll
+        for (int v = 0; v < NW - 1; ++v) {
+            if (v < w) {
+                const float pv = sFP[v * CB + j * VEC + e], ev = sFE[v * CB + j * VEC + e];
+                we = ev + pv * we;
+                wp = wp * pv;
+            }
+        }
+        XE[e] = XE[e] + XP[e] * we;
+        XP[e] = XP[e] * wp;
+        E[e] = XE[e] + XP[e] * cin[e];
+    }
 
     // ---- re-run the forward per step; readout backward; keep gE and the gate factor ----
     float Gr[L][VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) E[e] = sE[slot][j * VEC + e];
-#pragma unroll
     for (int i = 0; i < L; ++i) {
-        const bool ok = lane_ok && t0 + i < p.T;
+        const bool ok = FULL || (lane_ok && t0 + i < p.T);
         float Eprev[VEC];
         float ss = 0.0f;
 #pragma unroll
@@ -162,7 +199,10 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
             const float su = MODE == kDirect ? U_[i][e] : S_[i][e] * U_[i][e];
             V_[i][e] = MODE == kDirect ? Eprev[e] * su : (Eprev[e] - V_[i][e]) * su;
         }
-        if (ok) st16(p.dq, base + i * p.C, ES, pack<T>(dqv));
+        if constexpr (FULL)
+            stbuf(static_cast<char*>(p.dq) + row0 + i * rstride, voff, pack<T>(dqv));
+        else if (ok)
+            st16(p.dq, base + i * p.C, ES, pack<T>(dqv));
     }
 
     // ---- reverse fold of the thread's steps: lam_out = P * lam_in + E ----
@@ -177,45 +217,65 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         P[e] = pr;
         E[e] = er;
     }
-    __syncthreads();  // every thread has read its forward prefix from sE
+    wave_scan_rev<NCL, SPW, VEC>(P, E, sw);  // (P, E): slots sw..SPW-1 of this wave
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-        sP[slot][j * VEC + e] = P[e];
-        sE[slot][j * VEC + e] = E[e];
+        XP[e] = __shfl_down(P[e], NCL, kWave);
+        XE[e] = __shfl_down(E[e], NCL, kWave);
+        if (sw == SPW - 1) {
+            XP[e] = 1.0f;
+            XE[e] = 0.0f;
+        }
+        if (sw == 0) {
+            sRP[w * CB + j * VEC + e] = P[e];
+            sRE[w * CB + j * VEC + e] = E[e];
+        }
     }
     __syncthreads();
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        float ap = 1.0f, ae = 0.0f;  // map from the tile's right edge to this wave's right edge
+#pragma unroll
+        for (int v = NW - 1; v > 0; --v) {
+            if (v > w) {
+                const float pv = sRP[v * CB + j * VEC + e], ev = sRE[v * CB + j * VEC + e];
+                ae = ev + pv * ae;
+                ap = pv * ap;
+            }
+        }
+        XE[e] = XE[e] + XP[e] * ae;
+        XP[e] = XP[e] * ap;
+    }
 
-    if (tid < kWave) {
+    // ---- reverse look-back across tiles, by wave 0 (lane = channel) ----
+    if (w == 0) {
 #pragma unroll
         for (int k = 0; k < G::CPL; ++k) {
-            const int ch = tid + k * kWave;
+            const int ch = (tid % kWave) + k * kWave;
             float tp = 1.0f, te = 0.0f;
-#pragma unroll 8
-            for (int s = S - 1; s >= 0; --s) {
-                const float ps = sP[s][ch], es = sE[s][ch];
-                sP[s][ch] = tp;  // map from the tile's right edge to slot s's right edge
-                sE[s][ch] = te;
-                te = ps * te + es;
-                tp = ps * tp;
+#pragma unroll
+            for (int v = NW - 1; v >= 0; --v) {
+                const float pv = sRP[v * CB + ch], ev = sRE[v * CB + ch];
+                te = ev + pv * te;
+                tp = pv * tp;
             }
             const int64_t gl = (int64_t)cb * CB + ch;
             float carry = 0.0f;
-            if (gl < p.nLanes) {
+            if (FULL || gl < p.nLanes) {
                 uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
                 if (tile == p.nTiles - 1) {
                     carry = p.dET ? p.dET[gl] : 0.0f;
                 } else {
                     publish(X, tagAgg, te);
                     publish(p.flagY + (int64_t)tile * p.nLanes + gl, tagAgg, tp);
-                    carry = look_back(p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc, p.hdr);
+                    carry = look_back(p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc,
+                                      p.hdr);
                 }
                 const float lam_out = te + tp * carry;
                 publish(X, tagInc, lam_out);
                 if (tile == 0 && p.de0) p.de0[gl] = lam_out;
             }
-            // fold the carry into every slot's entry value
-#pragma unroll 8
-            for (int s = 0; s < S; ++s) sE[s][ch] = sE[s][ch] + sP[s][ch] * carry;
+            sCarry[ch] = carry;
         }
     }
     __syncthreads();
@@ -223,10 +283,10 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     // ---- reverse recurrence over the thread's steps; gate and value gradients ----
     float lam[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) lam[e] = sE[slot][j * VEC + e];
+    for (int e = 0; e < VEC; ++e) lam[e] = XE[e] + XP[e] * sCarry[j * VEC + e];
 #pragma unroll
     for (int i = L - 1; i >= 0; --i) {
-        const bool ok = lane_ok && t0 + i < p.T;
+        const bool ok = FULL || (lane_ok && t0 + i < p.T);
         float dav[VEC], dvv[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
@@ -235,11 +295,37 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
             dav[e] = dE * V_[i][e];
             dvv[e] = MODE == kDirect ? dE : dE * U_[i][e];
         }
-        if (ok) {
+        if constexpr (FULL) {
+            stbuf(static_cast<char*>(p.da) + row0 + i * rstride, voff, pack<T>(dav));
+            stbuf(static_cast<char*>(p.dv) + row0 + i * rstride, voff, pack<T>(dvv));
+        } else if (ok) {
             st16(p.da, base + i * p.C, ES, pack<T>(dav));
             st16(p.dv, base + i * p.C, ES, pack<T>(dvv));
         }
     }
+}
+
+template <typename T, int MODE, int DH, int L, int NT>
+__global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
+    using G = Geom<T, DH, L, NT>;
+    constexpr int CB = G::CB, TT = G::TT, NW = G::NW;
+    __shared__ float sFP[NW * CB];  // per-wave forward aggregate pairs
+    __shared__ float sFE[NW * CB];
+    __shared__ float sRP[NW * CB];  // per-wave reverse aggregate maps
+    __shared__ float sRE[NW * CB];
+    __shared__ float sCarry[CB];
+
+    uint32_t rtile, cb;
+    tile_of(blockIdx.x, p.nCB, rtile, cb);
+    const uint32_t tile = p.nTiles - 1 - rtile;  // the backward walks tiles from the end
+    // full: every step and lane of the tile exists, its channel block lies in one batch row,
+    // and the tile's byte span fits the 32-bit lane offsets
+    const bool full = (int64_t)(tile + 1) * TT <= p.T && (int64_t)(cb + 1) * CB <= p.nLanes &&
+                      p.C % CB == 0 && (int64_t)TT * p.C * (int64_t)sizeof(T) < (int64_t(1) << 31);
+    if (full)
+        bwd_tile<T, MODE, DH, L, NT, true>(p, tile, cb, sFP, sFE, sRP, sRE, sCarry);
+    else
+        bwd_tile<T, MODE, DH, L, NT, false>(p, tile, cb, sFP, sFE, sRP, sRE, sCarry);
 }
 
 template <typename T, int MODE, int DH>

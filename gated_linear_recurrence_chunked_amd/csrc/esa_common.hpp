@@ -12,19 +12,20 @@
 //   tile     a workgroup owns one channel block over TT = S * L time steps: S time slots
 //            of L consecutive steps, one slot per row of NCL threads.
 //   level 1  each thread folds its L steps in registers into one pair per channel.
-//   level 2  slot pairs go through LDS; one wave scans them in order, lane = channel.
+//   level 2  slot pairs are scanned across the slots of each wave with lane shuffles, then
+//            across the waves of the workgroup through LDS.
 //   level 3  tiles of one channel block are chained by a decoupled look-back: a tile
 //            publishes its aggregate pair, then walks back over earlier tiles' published
 //            pairs until it meets an inclusive value, then publishes its own inclusive
 //            value.
 //
-// Tile order.  Workgroup IDs are tile-major (id = tile * nCB + channel block; the backward
-// numbers tiles from the end), so a tile only ever waits on tiles with smaller IDs.  The
-// hardware starts the workgroups of one dispatch in increasing ID order on each XCD, so the
-// lowest unfinished workgroup is always resident and everything it waits on has finished:
-// the chain always makes progress, with no atomic counter per workgroup (a single-address
-// device atomic serialises at tens of ns each, which at 2^18 tiles would cost milliseconds).
-// Every wait is also bounded (see look_back), so even a broken chain ends.
+// Tile order.  Workgroup IDs are tile-major within each XCD (see tile_of; the backward numbers
+// tiles from the end), so a tile only ever waits on tiles with smaller IDs.  The hardware
+// starts the workgroups of one dispatch in increasing ID order on each XCD, so the lowest
+// unfinished workgroup is always resident and everything it waits on has finished: the chain
+// always makes progress, with no atomic counter per workgroup (a single-address device atomic
+// serialises at tens of ns each, which at 2^18 tiles would cost milliseconds).  Every wait is
+// also bounded (see look_back), so even a broken chain ends.
 //
 // Look-back words are 64-bit (tag, fp32 value) pairs written and read with single-copy
 // atomic 64-bit accesses at agent scope, so no fence is needed between a value and its
@@ -67,8 +68,11 @@ struct Geom {
     static constexpr int S = NT / NCL;            // time slots per tile
     static constexpr int TT = S * L;              // time steps per tile
     static constexpr int HL = DH / VEC;           // threads per head
-    static constexpr int CPL = CB / kWave;        // channels per lane of the scan wave
+    static constexpr int CPL = CB / kWave;        // channels per lane of the look-back wave
+    static constexpr int NW = NT / kWave;         // waves per workgroup
+    static constexpr int SPW = kWave / NCL;       // time slots per wave
     static_assert(CB % VEC == 0 && NT % NCL == 0 && S >= 1, "bad tile geometry");
+    static_assert(kWave % NCL == 0 && CB % kWave == 0, "a wave holds whole rows of a block");
     static_assert(HL >= 1 && (HL & (HL - 1)) == 0 && HL <= kWave, "head must be 2^k lanes");
 };
 
@@ -230,6 +234,31 @@ __device__ __forceinline__ uint4 pack<__bf16>(const float* x) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Raw buffer access for tiles that lie inside one batch row: a workgroup-uniform resource
+// (base = the tile's first element in this channel block) in scalar registers, one 32-bit
+// lane offset shared by every step, and the step's row offset as a scalar offset.  This
+// replaces a 64-bit vector address per load or store.  Word 3 is the raw 32-bit-element
+// format of gfx9-family buffer resources; the range check is never reached (offsets stay
+// below 2^31 by construction).
+typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
+constexpr int kBufWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                             kBufWord3);
+}
+__device__ __forceinline__ uint4 ldbuf(__amdgpu_buffer_rsrc_t r, uint32_t voff, int32_t soff) {
+    const v4u_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0);
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+// Stores take their row offset in the resource base and a constant scalar offset of 0.  A
+// 16-byte buffer store that names a scalar-register offset gets no wait state before the
+// next instruction overwrites its data registers, and on gfx950 the store can then write
+// the new value for some lanes (seen as corrupted dq rows); with a constant offset the
+// compiler keeps the required gap.
+__device__ __forceinline__ void stbuf(const void* row_base, uint32_t voff, const uint4& v) {
+    const v4u_t x = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(x, make_rsrc(row_base), (int)voff, 0, 0);
+}
 __device__ __forceinline__ uint4 ld16(const void* base, int64_t elem_off, int esize) {
     const char* p = static_cast<const char*>(base) + elem_off * esize;
     return *reinterpret_cast<const uint4*>(p);
@@ -251,13 +280,59 @@ __device__ __forceinline__ void gate(float a, float& s, float& u) {
     u = e * s;
 }
 
-// Sum over the HL consecutive, aligned threads that hold one head (a butterfly, so every
-// thread of the head receives the total).
+// Sum over the HL consecutive, aligned threads that hold one head; every thread of the head
+// receives the total.  Up to 16 threads (one DPP row) the butterfly uses DPP lane moves:
+// swap neighbours, swap pairs, mirror each half row, mirror the row.  Wider heads use
+// cross-row shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
 template <int HL>
 __device__ __forceinline__ float head_sum(float x) {
+    if constexpr (HL >= 2) x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
+    if constexpr (HL >= 4) x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
+    if constexpr (HL >= 8) x = dpp_add<0x141>(x);  // row_half_mirror
+    if constexpr (HL >= 16) x = dpp_add<0x140>(x); // row_mirror
 #pragma unroll
-    for (int m = 1; m < HL; m <<= 1) x += __shfl_xor(x, m, kWave);
+    for (int m = 16; m < HL; m <<= 1) x += __shfl_xor(x, m, kWave);
     return x;
+}
+
+// Inclusive scan of the pairs (P, E) over the SPW time slots of one wave (lane = slot * NCL +
+// channel lane), per channel: forward order composes earlier slots first,
+// (P1, E1) o (P2, E2) = (P1 P2, E2 + P2 E1).
+template <int NCL, int SPW, int VEC>
+__device__ __forceinline__ void wave_scan_fwd(float (&P)[VEC], float (&E)[VEC], int sw) {
+#pragma unroll
+    for (int d = 1; d < SPW; d <<= 1) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float pp = __shfl_up(P[e], d * NCL, kWave);
+            const float ep = __shfl_up(E[e], d * NCL, kWave);
+            if (sw >= d) {
+                E[e] = E[e] + P[e] * ep;
+                P[e] = P[e] * pp;
+            }
+        }
+    }
+}
+// The reverse-time counterpart: maps lam_out = P lam_in + E with lam_in arriving from the
+// later slot, composed from the right: slot s then s + d gives (P_s P_{s+d}, E_s + P_s E_{s+d}).
+template <int NCL, int SPW, int VEC>
+__device__ __forceinline__ void wave_scan_rev(float (&P)[VEC], float (&E)[VEC], int sw) {
+#pragma unroll
+    for (int d = 1; d < SPW; d <<= 1) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float pn = __shfl_down(P[e], d * NCL, kWave);
+            const float en = __shfl_down(E[e], d * NCL, kWave);
+            if (sw + d < SPW) {
+                E[e] = E[e] + P[e] * en;
+                P[e] = P[e] * pn;
+            }
+        }
+    }
 }
 
 __device__ __forceinline__ uint64_t tag_word(uint32_t tag, float v) {
@@ -314,6 +389,24 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
             }
         }
         __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// Workgroup -> (tile row, channel block).  Workgroup i runs on XCD i mod 8.  When the channel
+// blocks split evenly over the 8 XCDs, XCD x owns the contiguous channel blocks
+// [x nCB/8, (x+1) nCB/8) -- whole rows of the [B, T, H, Dh] tensors -- and walks them tile row
+// by tile row, so the 128-byte pieces of one row that neighbouring workgroups read reach
+// memory from one XCD, and each look-back chain stays inside one XCD.  Otherwise the order
+// is plain tile-major.  Either way a tile's predecessor in its chain has a smaller workgroup
+// ID, which is all the progress argument needs, whatever the real XCD placement.
+__device__ __forceinline__ void tile_of(uint32_t wg, uint32_t nCB, uint32_t& row, uint32_t& cb) {
+    if ((nCB & 7u) == 0u) {
+        const uint32_t x = wg & 7u, m = wg >> 3, nx = nCB >> 3;
+        row = m / nx;
+        cb = x * nx + (m - row * nx);
+    } else {
+        row = wg / nCB;
+        cb = wg - row * nCB;
     }
 }
 

@@ -5,53 +5,72 @@
 // and controlled ESA); readout y = q * Norm(E_t) from the same section, with Norm read as
 // per-head RMSNorm (eps 1e-6, no gain); composition over the sequence and the compact final
 // state: page "Entangled State Attention", section "[ ARCHITECTURE ]".
+//
+// Loads are issued without branches (rows past the end of the sequence and lanes past the
+// end of the batch load a clamped, valid address and are masked afterwards), so all of a
+// thread's loads are in flight at once; a branch between two loads would make the compiler
+// drain the first before issuing the next.  Tiles that are entirely inside the problem (all
+// but the ragged last tile row and channel block) take a path with no per-element masking,
+// addressing every load as a workgroup-uniform base plus one 32-bit lane offset.
 #include "esa_common.hpp"
 
 namespace esa {
 
-template <typename T, int MODE, int DH, int L, int NT>
-__global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
+template <typename T, int MODE, int DH, int L, int NT, bool READOUT, bool FULL>
+__device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint32_t cb,
+                                         float* sWP, float* sWE, float* sCarry) {
     using G = Geom<T, DH, L, NT>;
-    constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, S = G::S, HL = G::HL;
+    constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, HL = G::HL;
     constexpr int TT = G::TT;
     constexpr int ES = sizeof(T);
-
-    __shared__ float sP[S][CB];
-    __shared__ float sE[S][CB];
-    __shared__ float sCarry[CB];
-
-    const uint32_t wg = blockIdx.x;
-    const uint32_t tile = wg / p.nCB;
-    const uint32_t cb = wg - tile * p.nCB;
     const uint32_t tagAgg = make_tag(p.epoch, kTagAgg);
     const uint32_t tagInc = make_tag(p.epoch, kTagInc);
-    const bool readout = p.y != nullptr;
 
     const int tid = threadIdx.x;
     const int j = tid % NCL;
     const int slot = tid / NCL;
-    const int64_t lane0 = (int64_t)cb * CB + j * VEC;  // first flattened (b, h, d) lane
-    const bool lane_ok = lane0 < p.nLanes;
+    const int64_t lane0 = (int64_t)cb * CB + j * VEC;
+    const bool lane_ok = FULL || lane0 < p.nLanes;
     const int64_t b = lane_ok ? lane0 / p.C : 0;
     const int64_t c = lane_ok ? lane0 - b * p.C : 0;
     const int64_t t0 = (int64_t)tile * TT + (int64_t)slot * L;
     const int64_t base = (b * p.T + t0) * p.C + c;
 
-    // ---- load the thread's L steps (all loads issued before any use) ----
+    // ---- issue every load of the thread's L steps, branch-free ----
     uint4 ra[L], rv[L], rq[L];
+    // full tiles: buffer resources at the tile's first element, one lane offset, row offsets
+    const int64_t g0 = (int64_t)cb * CB;
+    const int64_t bw = g0 / p.C;
+    const int64_t row0 = ((bw * p.T + (int64_t)tile * TT) * p.C + (g0 - bw * p.C)) * ES;
+    const uint32_t voff = (uint32_t)(((int64_t)slot * L * p.C + j * VEC) * ES);
+    const int32_t rstride = (int32_t)(p.C * ES);
+    if constexpr (FULL) {
+        const auto rs_a = make_rsrc(static_cast<const char*>(p.a) + row0);
+        const auto rs_v = make_rsrc(static_cast<const char*>(p.v) + row0);
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-        ra[i] = make_uint4(0, 0, 0, 0);
-        rv[i] = make_uint4(0, 0, 0, 0);
-        rq[i] = make_uint4(0, 0, 0, 0);
-        if (lane_ok && t0 + i < p.T) {
-            ra[i] = ld16(p.a, base + i * p.C, ES);
-            rv[i] = ld16(p.v, base + i * p.C, ES);
-            if (readout) rq[i] = ld16(p.q, base + i * p.C, ES);
+        for (int i = 0; i < L; ++i) {
+            ra[i] = ldbuf(rs_a, voff, i * rstride);
+            rv[i] = ldbuf(rs_v, voff, i * rstride);
+            if constexpr (READOUT) rq[i] = ldbuf(make_rsrc(static_cast<const char*>(p.q) + row0), voff, i * rstride);
+            else rq[i] = make_uint4(0, 0, 0, 0);
+        }
+    } else {
+        // ragged tile: rows past the end and lanes past the batch load a clamped, valid
+        // address and are masked below
+        const int64_t lc = lane_ok ? lane0 : 0;
+        const int64_t bc = lc / p.C, cc = lc - bc * p.C;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const int64_t t = t0 + i < p.T ? t0 + i : p.T - 1;
+            const int64_t off = (bc * p.T + t) * p.C + cc;
+            ra[i] = ld16(p.a, off, ES);
+            rv[i] = ld16(p.v, off, ES);
+            if constexpr (READOUT) rq[i] = ld16(p.q, off, ES);
+            else rq[i] = make_uint4(0, 0, 0, 0);
         }
     }
 
-    // ---- level 1: gates and the thread's own fold ----
+    // ---- level 1: gates and the thread's own fold (identity pair where masked) ----
     float A[L][VEC], Bt[L][VEC];
     float P[VEC], E[VEC];
 #pragma unroll
@@ -61,7 +80,7 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-        const bool ok = lane_ok && t0 + i < p.T;
+        const bool ok = FULL || (lane_ok && t0 + i < p.T);
         float av[VEC], vv[VEC];
         unpack<T>(ra[i], av);
         unpack<T>(rv[i], vv);
@@ -69,45 +88,72 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
         for (int e = 0; e < VEC; ++e) {
             float s, u;
             gate(av[e], s, u);
+            const float bt = MODE == kDirect ? vv[e] : u * vv[e];
             A[i][e] = ok ? s : 1.0f;
-            Bt[i][e] = ok ? (MODE == kDirect ? vv[e] : u * vv[e]) : 0.0f;
+            Bt[i][e] = ok ? bt : 0.0f;
             E[e] = A[i][e] * E[e] + Bt[i][e];
             P[e] = P[e] * A[i][e];
         }
     }
 
-    // ---- level 2: slot pairs through LDS, scanned in order by wave 0 ----
+    // ---- level 2: scan over the slots of each wave, then across the waves ----
+    constexpr int SPW = G::SPW, NW = G::NW;
+    const int w = tid / kWave;
+    const int sw = (tid % kWave) / NCL;
+    wave_scan_fwd<NCL, SPW, VEC>(P, E, sw);  // (P, E): slots 0..sw of this wave
+    float XP[VEC], XE[VEC];                  // exclusive prefix of this thread's slot
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-        sP[slot][j * VEC + e] = P[e];
-        sE[slot][j * VEC + e] = E[e];
+        XP[e] = __shfl_up(P[e], NCL, kWave);
+        XE[e] = __shfl_up(E[e], NCL, kWave);
+        if (sw == 0) {
+            XP[e] = 1.0f;
+            XE[e] = 0.0f;
+        }
+        if (sw == SPW - 1) {  // wave aggregate
+            sWP[w * CB + j * VEC + e] = P[e];
+            sWE[w * CB + j * VEC + e] = E[e];
+        }
     }
     __syncthreads();
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        float wp = 1.0f, we = 0.0f;  // composition of the earlier waves
+#pragma unroll
+        for (int v = 0; v < NW - 1; ++v) {
+            if (v < w) {
+                const float pv = sWP[v * CB + j * VEC + e], ev = sWE[v * CB + j * VEC + e];
+                we = ev + pv * we;
+                wp = wp * pv;
+            }
+        }
+        XE[e] = XE[e] + XP[e] * we;
+        XP[e] = XP[e] * wp;
+    }
 
-    if (tid < kWave) {
+    // ---- level 3: decoupled look-back across tiles, by wave 0 (lane = channel) ----
+    if (w == 0) {
 #pragma unroll
         for (int k = 0; k < G::CPL; ++k) {
-            const int ch = tid + k * kWave;
+            const int ch = (tid % kWave) + k * kWave;
             float tp = 1.0f, te = 0.0f;
-#pragma unroll 8
-            for (int s = 0; s < S; ++s) {
-                const float ps = sP[s][ch], es = sE[s][ch];
-                sP[s][ch] = tp;  // exclusive prefix of slot s within the tile
-                sE[s][ch] = te;
-                te = ps * te + es;
-                tp = tp * ps;
+#pragma unroll
+            for (int v = 0; v < NW; ++v) {
+                const float pv = sWP[v * CB + ch], ev = sWE[v * CB + ch];
+                te = ev + pv * te;
+                tp = tp * pv;
             }
-            // ---- level 3: decoupled look-back across tiles ----
             const int64_t gl = (int64_t)cb * CB + ch;
             float carry = 0.0f;
-            if (gl < p.nLanes) {
+            if (FULL || gl < p.nLanes) {
                 uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
                 if (tile == 0) {
                     carry = p.e0 ? p.e0[gl] : 0.0f;
                 } else {
                     publish(X, tagAgg, te);
                     publish(p.flagY + (int64_t)tile * p.nLanes + gl, tagAgg, tp);
-                    carry = look_back(p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg, tagInc, p.hdr);
+                    carry = look_back(p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg, tagInc,
+                                      p.hdr);
                 }
                 publish(X, tagInc, te + tp * carry);
             }
@@ -118,29 +164,29 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
 
     // ---- carry in, re-run the recurrence, readout ----
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-        const int ch = j * VEC + e;
-        E[e] = sE[slot][ch] + sP[slot][ch] * sCarry[ch];
-    }
+    for (int e = 0; e < VEC; ++e) E[e] = XE[e] + XP[e] * sCarry[j * VEC + e];
     const int64_t ckbase = b * p.nck;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
         const int64_t t = t0 + i;
-        const bool ok = lane_ok && t < p.T;
+        const bool ok = FULL || (lane_ok && t < p.T);
         float ss = 0.0f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             E[e] = A[i][e] * E[e] + Bt[i][e];
             ss += E[e] * E[e];
         }
-        if (readout) {
+        if constexpr (READOUT) {
             ss = head_sum<HL>(ss);
             const float r = __builtin_amdgcn_rsqf(ss * (1.0f / DH) + kEps);
             float qv[VEC], yv[VEC];
             unpack<T>(rq[i], qv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) yv[e] = qv[e] * (E[e] * r);
-            if (ok) st16(p.y, base + i * p.C, ES, pack<T>(yv));
+            if constexpr (FULL)
+                stbuf(static_cast<char*>(p.y) + row0 + i * rstride, voff, pack<T>(yv));
+            else if (ok)
+                st16(p.y, base + i * p.C, ES, pack<T>(yv));
         }
         if (ok && p.ckpt && (((t + 1) % kCkptChunk) == 0 || t == p.T - 1)) {
             float* dst = p.ckpt + (ckbase + t / kCkptChunk) * p.C + c;
@@ -157,10 +203,34 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     }
 }
 
+template <typename T, int MODE, int DH, int L, int NT, bool READOUT>
+__global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
+    using G = Geom<T, DH, L, NT>;
+    constexpr int CB = G::CB, TT = G::TT, NW = G::NW;
+    __shared__ float sWP[NW * CB];  // per-wave aggregate pairs
+    __shared__ float sWE[NW * CB];
+    __shared__ float sCarry[CB];
+
+    uint32_t tile, cb;
+    tile_of(blockIdx.x, p.nCB, tile, cb);
+    // full: every step and lane of the tile exists and its channel block lies in one batch row
+    // (and the tile's byte span fits the 32-bit lane offsets)
+    const bool full = (int64_t)(tile + 1) * TT <= p.T && (int64_t)(cb + 1) * CB <= p.nLanes &&
+                      p.C % CB == 0 && (int64_t)TT * p.C * (int64_t)sizeof(T) < (int64_t(1) << 31);
+    if (full)
+        fwd_tile<T, MODE, DH, L, NT, READOUT, true>(p, tile, cb, sWP, sWE, sCarry);
+    else
+        fwd_tile<T, MODE, DH, L, NT, READOUT, false>(p, tile, cb, sWP, sWE, sCarry);
+}
+
 template <typename T, int MODE, int DH>
 hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
     using C = FwdCfg<T, DH>;
-    hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT>), dim3(p.nCB * p.nTiles), dim3(C::NT), 0, s, p);
+    const dim3 grid(p.nCB * p.nTiles), block(C::NT);
+    if (p.y)
+        hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, true>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, false>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 

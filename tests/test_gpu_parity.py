@@ -62,6 +62,11 @@ SHAPES = [
     (5, 300, 1, 16),
     (2, 777, 2, 128),
     (1, 256, 2, 16),
+    # channel-block counts divisible by 8: the XCD-aware tile order
+    (8, 300, 1, 64),
+    (4, 130, 4, 32),
+    (2, 200, 8, 128),
+    (16, 257, 2, 16),
 ]
 DTYPE_MODE = [("f32", "direct"), ("f32", "controlled"), ("f16", "controlled"), ("f16", "direct"),
               ("bf16", "direct"), ("bf16", "controlled")]
