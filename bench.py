@@ -24,6 +24,38 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+COUNTERS = os.path.join(ROOT, "profiles", "esa_scan_long64k_f16_hbm_counters.txt")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources (name + bytes, sorted), to tell whether counters taken
+    earlier still describe the kernels built now."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_linear_recurrence_chunked_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's readings), or None when the summary is
+    missing or was taken on different kernel sources."""
+    try:
+        text = open(COUNTERS).read()
+    except OSError:
+        return None
+    vals = dict(line.strip().split(": ", 1) for line in text.splitlines()
+                if line.strip().startswith(("kernel_source_sha256:", f"{kernel}_traffic_bytes:")))
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    v = vals.get(f"{kernel}_traffic_bytes")
+    return int(float(v)) if v else None
 
 
 def parse():
@@ -253,7 +285,7 @@ def main():
         result["roofline"] = {"kernel": f"esa {dom}_kernel (f16, controlled, Dh=64)",
                               "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                              "traffic": None,
+                              "traffic": measured_traffic(dom),
                               "algorithmic_bytes_per_launch": train[f"{dom}_bytes"],
                               "avg_launch_ms": round(train[f"{dom}_ms"], 4)}
         result["kernels"] = {
