@@ -1,0 +1,104 @@
+"""Autograd and layer wrappers over the library's scan.
+
+``esa_scan(a, v, q, init_state=None, mode)`` is differentiable: its forward is
+``esa_scan_fwd`` (keeping the fp32 state checkpoint), its backward ``esa_scan_bwd``.
+
+``ESALayer`` is the ESA sequence layer of page "entangled-state-attention 0.1.0", section
+"Core idea": gate logits, values and queries are projections of x, the scan runs in the
+library, and the output projection maps the readout back:
+
+    a = x W_A,  v = x W_V,  q = x W_Q                    (plain GEMMs, no bias)
+    y_t = W_O (q_t * Norm(E_t)),  E_t = s_t E_{t-1} + B_t  (library kernels)
+
+with the heads and the prefill / decode_step interface of page "Entangled State
+Attention", section "[ QUICK START ]" (``esa = ESA(embd=512, head=8)``,
+``out, state = esa.prefill(prompt)``, ``out, state = esa.decode_step(token, state)``).
+The projections are ordinary library matrix products; everything of the recurrence runs
+in the HIP kernels.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import binding
+
+
+class _ScanFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, a, v, q, init_state, mode):
+        y, final_state, ckpt = binding.scan_fwd(a, v, q, init_state, mode=mode, return_ckpt=True)
+        ctx.mode = mode
+        ctx.has_init = init_state is not None
+        ctx.save_for_backward(a, v, q, init_state if init_state is not None else ckpt, ckpt)
+        return y, final_state
+
+    @staticmethod
+    def backward(ctx, dy, d_final):
+        a, v, q, init_or_ckpt, ckpt = ctx.saved_tensors
+        init_state = init_or_ckpt if ctx.has_init else None
+        if dy is None:
+            dy = torch.zeros_like(a)
+        da, dv, dq, d_init = binding.scan_bwd(a, v, q, dy.contiguous(), init_state,
+                                              None if d_final is None else d_final.contiguous(),
+                                              ckpt=ckpt, mode=ctx.mode)
+        return da, dv, dq, (d_init if ctx.has_init else None), None
+
+
+def esa_scan(a, v, q, init_state=None, mode="controlled"):
+    """Differentiable scan: returns (y [B,T,H,Dh], final_state fp32 [B,H,Dh])."""
+    return _ScanFn.apply(a, v, q, init_state, mode)
+
+
+class ESALayer(torch.nn.Module):
+    """ESA layer: projections, the library's gated scan with per-head RMSNorm readout, and the
+    output projection.  ``dtype`` is the storage dtype of the scan's inputs and outputs."""
+
+    def __init__(self, embd: int, head: int, mode: str = "controlled", dtype=torch.float16,
+                 device=None):
+        super().__init__()
+        if embd % head:
+            raise ValueError("embd must be a multiple of head")
+        self.embd, self.head, self.dh = embd, head, embd // head
+        if self.dh not in (16, 32, 64, 128):
+            raise ValueError("head dimension embd / head must be 16, 32, 64 or 128")
+        self.mode = mode
+        kw = dict(device=device, dtype=dtype)
+        self.W_A = torch.nn.Parameter(torch.empty(embd, embd, **kw))
+        self.W_V = torch.nn.Parameter(torch.empty(embd, embd, **kw))
+        self.W_Q = torch.nn.Parameter(torch.empty(embd, embd, **kw))
+        self.W_O = torch.nn.Parameter(torch.empty(embd, embd, **kw))
+        self.reset_parameters()
+
+    def reset_parameters(self):
+        bound = 1.0 / math.sqrt(self.embd)
+        for w in (self.W_A, self.W_V, self.W_Q, self.W_O):
+            torch.nn.init.uniform_(w, -bound, bound)
+
+    def _project(self, x):
+        shp = x.shape[:-1] + (self.head, self.dh)
+        a = (x @ self.W_A).reshape(shp)
+        v = (x @ self.W_V).reshape(shp)
+        q = (x @ self.W_Q).reshape(shp)
+        return a, v, q
+
+    def forward(self, x, init_state=None, return_state=False):
+        """x: [B, T, embd] -> y [B, T, embd] (and the fp32 state [B, head, dh])."""
+        a, v, q = self._project(x)
+        r, state = esa_scan(a.contiguous(), v.contiguous(), q.contiguous(), init_state,
+                            mode=self.mode)
+        y = r.reshape(x.shape) @ self.W_O
+        return (y, state) if return_state else y
+
+    def prefill(self, x, state=None):
+        """Full-sequence pass that also returns the compact recurrent state."""
+        return self.forward(x, init_state=state, return_state=True)
+
+    @torch.no_grad()
+    def decode_step(self, x_t, state):
+        """One token: x_t [B, embd]; state fp32 [B, head, dh] is updated in place."""
+        a, v, q = self._project(x_t)
+        r = binding.state_step(a.contiguous(), v.contiguous(), q.contiguous(), state,
+                               mode=self.mode)
+        return r.reshape(x_t.shape) @ self.W_O, state

@@ -62,7 +62,9 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
 
 template <typename T, int MODE, int DH>
 hipError_t launch_step(const StepParams& p, hipStream_t s) {
-    constexpr int NT = 256;
+    // small workgroups: a decode step has few lanes (B*H*Dh / VEC threads), and one wave per
+    // workgroup spreads them over more CUs, which shortens the step (launch-latency-bound)
+    constexpr int NT = 64;
     constexpr int VEC = Storage<T>::VEC;
     const int64_t threads = (p.nLanes + VEC - 1) / VEC;
     const int64_t blocks = (threads + NT - 1) / NT;
