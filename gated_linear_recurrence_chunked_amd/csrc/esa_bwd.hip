@@ -24,11 +24,11 @@
 namespace esa {
 
 template <typename T, int MODE, int DH, int L, int NT, bool FULL>
-__device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint32_t cb, float* sFP,
-                                         float* sFE, float* sRP, float* sRE, float* sCarry) {
+__device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint32_t cb, float* sP,
+                                         float* sE, float* sWP, float* sWE, float* sCarry) {
     using G = Geom<T, DH, L, NT>;
     constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, HL = G::HL;
-    constexpr int TT = G::TT, SPW = G::SPW, NW = G::NW;
+    constexpr int TT = G::TT;
     constexpr int ES = sizeof(T);
     const uint32_t tagAgg = make_tag(p.epoch, kTagAgg);
     const uint32_t tagInc = make_tag(p.epoch, kTagInc);
@@ -36,8 +36,6 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     const int tid = threadIdx.x;
     const int j = tid % NCL;
     const int slot = tid / NCL;
-    const int w = tid / kWave;
-    const int sw = (tid % kWave) / NCL;
     const int64_t lane0 = (int64_t)cb * CB + j * VEC;
     const bool lane_ok = FULL || lane0 < p.nLanes;
     const int64_t b = lane_ok ? lane0 / p.C : 0;
@@ -130,38 +128,17 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     }
 
     // ---- state entering this thread's steps: the checkpoint at the tile start, carried
-    //      through the earlier slots of the tile (two-level scan, no look-back needed) ----
-    wave_scan_fwd<NCL, SPW, VEC>(P, E, sw);
+    //      through the earlier slots of the tile (two-phase slot scan, no look-back needed) ----
+    const int w = tid / kWave;
+    float xp[G::CPL][G::SPW], xe[G::CPL][G::SPW];
     float XP[VEC], XE[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-        XP[e] = __shfl_up(P[e], NCL, kWave);
-        XE[e] = __shfl_up(E[e], NCL, kWave);
-        if (sw == 0) {
-            XP[e] = 1.0f;
-            XE[e] = 0.0f;
-        }
-        if (sw == SPW - 1) {
-            sFP[w * CB + j * VEC + e] = P[e];
-            sFE[w * CB + j * VEC + e] = E[e];
-        }
-    }
+    slots_phase_a<G, false>(P, E, sP, sE, sWP, sWE, xp, xe);
     __syncthreads();
+    slots_phase_b<G, false>(sP, sE, sWP, sWE, xp, xe);
+    __syncthreads();
+    read_exclusive<G>(sP, sE, XP, XE);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-        float wp = 1.0f, we = 0.0f;
-#pragma unroll
-        for (int v = 0; v < NW - 1; ++v) {
-            if (v < w) {
-                const float pv = sFP[v * CB + j * VEC + e], ev = sFE[v * CB + j * VEC + e];
-                we = ev + pv * we;
-                wp = wp * pv;
-            }
-        }
-        XE[e] = XE[e] + XP[e] * we;
-        XP[e] = XP[e] * wp;
-        E[e] = XE[e] + XP[e] * cin[e];
-    }
+    for (int e = 0; e < VEC; ++e) E[e] = XE[e] + XP[e] * cin[e];
 
     // ---- re-run the forward per step; readout backward; keep gE and the gate factor ----
     float Gr[L][VEC];
@@ -217,48 +194,19 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         P[e] = pr;
         E[e] = er;
     }
-    wave_scan_rev<NCL, SPW, VEC>(P, E, sw);  // (P, E): slots sw..SPW-1 of this wave
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-        XP[e] = __shfl_down(P[e], NCL, kWave);
-        XE[e] = __shfl_down(E[e], NCL, kWave);
-        if (sw == SPW - 1) {
-            XP[e] = 1.0f;
-            XE[e] = 0.0f;
-        }
-        if (sw == 0) {
-            sRP[w * CB + j * VEC + e] = P[e];
-            sRE[w * CB + j * VEC + e] = E[e];
-        }
-    }
+    // the slot arrays are reused: this thread's slot positions were last read by this thread,
+    // and the wave aggregates by every wave before the barrier above
+    slots_phase_a<G, true>(P, E, sP, sE, sWP, sWE, xp, xe);
     __syncthreads();
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-        float ap = 1.0f, ae = 0.0f;  // map from the tile's right edge to this wave's right edge
-#pragma unroll
-        for (int v = NW - 1; v > 0; --v) {
-            if (v > w) {
-                const float pv = sRP[v * CB + j * VEC + e], ev = sRE[v * CB + j * VEC + e];
-                ae = ev + pv * ae;
-                ap = pv * ap;
-            }
-        }
-        XE[e] = XE[e] + XP[e] * ae;
-        XP[e] = XP[e] * ap;
-    }
+    slots_phase_b<G, true>(sP, sE, sWP, sWE, xp, xe);
 
     // ---- reverse look-back across tiles, by wave 0 (lane = channel) ----
     if (w == 0) {
 #pragma unroll
         for (int k = 0; k < G::CPL; ++k) {
             const int ch = (tid % kWave) + k * kWave;
-            float tp = 1.0f, te = 0.0f;
-#pragma unroll
-            for (int v = NW - 1; v >= 0; --v) {
-                const float pv = sRP[v * CB + ch], ev = sRE[v * CB + ch];
-                te = ev + pv * te;
-                tp = pv * tp;
-            }
+            float tp, te;
+            tile_total<G, true>(sWP, sWE, ch, tp, te);
             const int64_t gl = (int64_t)cb * CB + ch;
             float carry = 0.0f;
             if (FULL || gl < p.nLanes) {
@@ -279,6 +227,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         }
     }
     __syncthreads();
+    read_exclusive<G>(sP, sE, XP, XE);
 
     // ---- reverse recurrence over the thread's steps; gate and value gradients ----
     float lam[VEC];
@@ -309,10 +258,10 @@ template <typename T, int MODE, int DH, int L, int NT>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     using G = Geom<T, DH, L, NT>;
     constexpr int CB = G::CB, TT = G::TT, NW = G::NW;
-    __shared__ float sFP[NW * CB];  // per-wave forward aggregate pairs
-    __shared__ float sFE[NW * CB];
-    __shared__ float sRP[NW * CB];  // per-wave reverse aggregate maps
-    __shared__ float sRE[NW * CB];
+    __shared__ __attribute__((aligned(16))) float sP[G::S * CB];  // per-slot pairs / maps
+    __shared__ __attribute__((aligned(16))) float sE[G::S * CB];
+    __shared__ float sWP[NW * CB];  // per-wave aggregates
+    __shared__ float sWE[NW * CB];
     __shared__ float sCarry[CB];
 
     uint32_t rtile, cb;
@@ -323,9 +272,9 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     const bool full = (int64_t)(tile + 1) * TT <= p.T && (int64_t)(cb + 1) * CB <= p.nLanes &&
                       p.C % CB == 0 && (int64_t)TT * p.C * (int64_t)sizeof(T) < (int64_t(1) << 31);
     if (full)
-        bwd_tile<T, MODE, DH, L, NT, true>(p, tile, cb, sFP, sFE, sRP, sRE, sCarry);
+        bwd_tile<T, MODE, DH, L, NT, true>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
     else
-        bwd_tile<T, MODE, DH, L, NT, false>(p, tile, cb, sFP, sFE, sRP, sRE, sCarry);
+        bwd_tile<T, MODE, DH, L, NT, false>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
 }
 
 template <typename T, int MODE, int DH>

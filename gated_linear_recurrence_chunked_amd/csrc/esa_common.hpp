@@ -12,8 +12,8 @@
 //   tile     a workgroup owns one channel block over TT = S * L time steps: S time slots
 //            of L consecutive steps, one slot per row of NCL threads.
 //   level 1  each thread folds its L steps in registers into one pair per channel.
-//   level 2  slot pairs are scanned across the slots of each wave with lane shuffles, then
-//            across the waves of the workgroup through LDS.
+//   level 2  slot pairs go through LDS: lane = channel of each wave scans that wave's slots,
+//            then the waves' aggregates are composed (slots_phase_a / slots_phase_b).
 //   level 3  tiles of one channel block are chained by a decoupled look-back: a tile
 //            publishes its aggregate pair, then walks back over earlier tiles' published
 //            pairs until it meets an inclusive value, then publishes its own inclusive
@@ -299,39 +299,115 @@ __device__ __forceinline__ float head_sum(float x) {
     return x;
 }
 
-// Inclusive scan of the pairs (P, E) over the SPW time slots of one wave (lane = slot * NCL +
-// channel lane), per channel: forward order composes earlier slots first,
-// (P1, E1) o (P2, E2) = (P1 P2, E2 + P2 E1).
-template <int NCL, int SPW, int VEC>
-__device__ __forceinline__ void wave_scan_fwd(float (&P)[VEC], float (&E)[VEC], int sw) {
+// Exclusive scan of the per-thread pairs over the S time slots of a tile, per channel, in
+// two phases through LDS (thread = slot * NCL + channel lane, VEC channels each; the slots
+// of wave w are w*SPW .. w*SPW+SPW-1).
+//
+// Phase A: every thread stores its pair; lane = channel of each wave then walks that wave's
+// SPW slots in order (backwards for the reverse scan), keeps each slot's exclusive pair within
+// the wave in registers, and stores the wave's aggregate.  No barrier is needed inside phase
+// A: a wave only reads what it has just written, and LDS serves one wave's requests in order.
+// Phase B (after a barrier): lane = channel composes the other waves' aggregates into the
+// wave prefix and stores each slot's exclusive pair for the whole tile.
+// Forward pairs compose earlier first, (P1, E1) o (P2, E2) = (P1 P2, E2 + P2 E1); reverse
+// maps lam_out = P lam_in + E compose the later side first; both reduce to the same update
+// (te, tp) <- (p te + e, tp p) in their own walking order.
+template <class G, bool REV>
+__device__ __forceinline__ void slots_phase_a(const float* P, const float* E, float* sP, float* sE,
+                                              float* sWP, float* sWE,
+                                              float (&xp)[G::CPL][G::SPW],
+                                              float (&xe)[G::CPL][G::SPW]) {
+    constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, SPW = G::SPW;
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+    const int j = tid % NCL, slot = tid / NCL;
 #pragma unroll
-    for (int d = 1; d < SPW; d <<= 1) {
+    for (int e = 0; e < VEC; e += 4) {
+        *reinterpret_cast<float4*>(sP + slot * CB + j * VEC + e) =
+            make_float4(P[e], P[e + 1], P[e + 2], P[e + 3]);
+        *reinterpret_cast<float4*>(sE + slot * CB + j * VEC + e) =
+            make_float4(E[e], E[e + 1], E[e + 2], E[e + 3]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const float pp = __shfl_up(P[e], d * NCL, kWave);
-            const float ep = __shfl_up(E[e], d * NCL, kWave);
-            if (sw >= d) {
-                E[e] = E[e] + P[e] * ep;
-                P[e] = P[e] * pp;
+    for (int k = 0; k < G::CPL; ++k) {
+        const int ch = lane + k * kWave;
+        float tp = 1.0f, te = 0.0f;
+#pragma unroll
+        for (int q = 0; q < SPW; ++q) {
+            const int sw = REV ? SPW - 1 - q : q;
+            const int s = w * SPW + sw;
+            const float ps = sP[s * CB + ch], es = sE[s * CB + ch];
+            xp[k][sw] = tp;
+            xe[k][sw] = te;
+            te = ps * te + es;
+            tp = tp * ps;
+        }
+        sWP[w * CB + ch] = tp;
+        sWE[w * CB + ch] = te;
+    }
+}
+
+template <class G, bool REV>
+__device__ __forceinline__ void slots_phase_b(float* sP, float* sE, const float* sWP,
+                                              const float* sWE, const float (&xp)[G::CPL][G::SPW],
+                                              const float (&xe)[G::CPL][G::SPW]) {
+    constexpr int CB = G::CB, SPW = G::SPW, NW = G::NW;
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+#pragma unroll
+    for (int k = 0; k < G::CPL; ++k) {
+        const int ch = lane + k * kWave;
+        float wp = 1.0f, we = 0.0f;  // the other waves on this slot's earlier side
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+            const int v = REV ? NW - 1 - q : q;
+            if (REV ? v > w : v < w) {
+                const float pv = sWP[v * CB + ch], ev = sWE[v * CB + ch];
+                we = pv * we + ev;
+                wp = wp * pv;
             }
+        }
+#pragma unroll
+        for (int sw = 0; sw < SPW; ++sw) {
+            const int s = w * SPW + sw;
+            sP[s * CB + ch] = xp[k][sw] * wp;
+            sE[s * CB + ch] = xe[k][sw] + xp[k][sw] * we;
         }
     }
 }
-// The reverse-time counterpart: maps lam_out = P lam_in + E with lam_in arriving from the
-// later slot, composed from the right: slot s then s + d gives (P_s P_{s+d}, E_s + P_s E_{s+d}).
-template <int NCL, int SPW, int VEC>
-__device__ __forceinline__ void wave_scan_rev(float (&P)[VEC], float (&E)[VEC], int sw) {
+
+// Composition of all waves' aggregates for channel ch: the tile's own pair / map.
+template <class G, bool REV>
+__device__ __forceinline__ void tile_total(const float* sWP, const float* sWE, int ch, float& tp,
+                                           float& te) {
+    tp = 1.0f;
+    te = 0.0f;
 #pragma unroll
-    for (int d = 1; d < SPW; d <<= 1) {
+    for (int q = 0; q < G::NW; ++q) {
+        const int v = REV ? G::NW - 1 - q : q;
+        const float pv = sWP[v * G::CB + ch], ev = sWE[v * G::CB + ch];
+        te = pv * te + ev;
+        tp = tp * pv;
+    }
+}
+
+// The tile-wide exclusive pair of this thread's slot, for its VEC channels.
+template <class G>
+__device__ __forceinline__ void read_exclusive(const float* sP, const float* sE, float* XP,
+                                               float* XE) {
+    const int j = threadIdx.x % G::NCL, slot = threadIdx.x / G::NCL;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const float pn = __shfl_down(P[e], d * NCL, kWave);
-            const float en = __shfl_down(E[e], d * NCL, kWave);
-            if (sw + d < SPW) {
-                E[e] = E[e] + P[e] * en;
-                P[e] = P[e] * pn;
-            }
-        }
+    for (int e = 0; e < G::VEC; e += 4) {
+        const float4 p = *reinterpret_cast<const float4*>(sP + slot * G::CB + j * G::VEC + e);
+        const float4 q = *reinterpret_cast<const float4*>(sE + slot * G::CB + j * G::VEC + e);
+        XP[e] = p.x;
+        XP[e + 1] = p.y;
+        XP[e + 2] = p.z;
+        XP[e + 3] = p.w;
+        XE[e] = q.x;
+        XE[e + 1] = q.y;
+        XE[e + 2] = q.z;
+        XE[e + 3] = q.w;
     }
 }
 

@@ -18,7 +18,8 @@ namespace esa {
 
 template <typename T, int MODE, int DH, int L, int NT, bool READOUT, bool FULL>
 __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint32_t cb,
-                                         float* sWP, float* sWE, float* sCarry) {
+                                         float* sP, float* sE, float* sWP, float* sWE,
+                                         float* sCarry) {
     using G = Geom<T, DH, L, NT>;
     constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, HL = G::HL;
     constexpr int TT = G::TT;
@@ -96,53 +97,20 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         }
     }
 
-    // ---- level 2: scan over the slots of each wave, then across the waves ----
-    constexpr int SPW = G::SPW, NW = G::NW;
+    // ---- level 2: slot pairs through LDS (within each wave, then across the waves) ----
     const int w = tid / kWave;
-    const int sw = (tid % kWave) / NCL;
-    wave_scan_fwd<NCL, SPW, VEC>(P, E, sw);  // (P, E): slots 0..sw of this wave
-    float XP[VEC], XE[VEC];                  // exclusive prefix of this thread's slot
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-        XP[e] = __shfl_up(P[e], NCL, kWave);
-        XE[e] = __shfl_up(E[e], NCL, kWave);
-        if (sw == 0) {
-            XP[e] = 1.0f;
-            XE[e] = 0.0f;
-        }
-        if (sw == SPW - 1) {  // wave aggregate
-            sWP[w * CB + j * VEC + e] = P[e];
-            sWE[w * CB + j * VEC + e] = E[e];
-        }
-    }
+    float xp[G::CPL][G::SPW], xe[G::CPL][G::SPW];
+    slots_phase_a<G, false>(P, E, sP, sE, sWP, sWE, xp, xe);
     __syncthreads();
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-        float wp = 1.0f, we = 0.0f;  // composition of the earlier waves
-#pragma unroll
-        for (int v = 0; v < NW - 1; ++v) {
-            if (v < w) {
-                const float pv = sWP[v * CB + j * VEC + e], ev = sWE[v * CB + j * VEC + e];
-                we = ev + pv * we;
-                wp = wp * pv;
-            }
-        }
-        XE[e] = XE[e] + XP[e] * we;
-        XP[e] = XP[e] * wp;
-    }
+    slots_phase_b<G, false>(sP, sE, sWP, sWE, xp, xe);
 
     // ---- level 3: decoupled look-back across tiles, by wave 0 (lane = channel) ----
     if (w == 0) {
 #pragma unroll
         for (int k = 0; k < G::CPL; ++k) {
             const int ch = (tid % kWave) + k * kWave;
-            float tp = 1.0f, te = 0.0f;
-#pragma unroll
-            for (int v = 0; v < NW; ++v) {
-                const float pv = sWP[v * CB + ch], ev = sWE[v * CB + ch];
-                te = ev + pv * te;
-                tp = tp * pv;
-            }
+            float tp, te;
+            tile_total<G, false>(sWP, sWE, ch, tp, te);
             const int64_t gl = (int64_t)cb * CB + ch;
             float carry = 0.0f;
             if (FULL || gl < p.nLanes) {
@@ -163,8 +131,12 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
     __syncthreads();
 
     // ---- carry in, re-run the recurrence, readout ----
+    {
+        float XP[VEC], XE[VEC];
+        read_exclusive<G>(sP, sE, XP, XE);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) E[e] = XE[e] + XP[e] * sCarry[j * VEC + e];
+        for (int e = 0; e < VEC; ++e) E[e] = XE[e] + XP[e] * sCarry[j * VEC + e];
+    }
     const int64_t ckbase = b * p.nck;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
@@ -206,7 +178,9 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
 template <typename T, int MODE, int DH, int L, int NT, bool READOUT>
 __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     using G = Geom<T, DH, L, NT>;
-    constexpr int CB = G::CB, TT = G::TT, NW = G::NW;
+    constexpr int CB = G::CB, TT = G::TT, NW = G::NW, S = G::S;
+    __shared__ __attribute__((aligned(16))) float sP[S * CB];  // per-slot pairs
+    __shared__ __attribute__((aligned(16))) float sE[S * CB];
     __shared__ float sWP[NW * CB];  // per-wave aggregate pairs
     __shared__ float sWE[NW * CB];
     __shared__ float sCarry[CB];
@@ -218,9 +192,9 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     const bool full = (int64_t)(tile + 1) * TT <= p.T && (int64_t)(cb + 1) * CB <= p.nLanes &&
                       p.C % CB == 0 && (int64_t)TT * p.C * (int64_t)sizeof(T) < (int64_t(1) << 31);
     if (full)
-        fwd_tile<T, MODE, DH, L, NT, READOUT, true>(p, tile, cb, sWP, sWE, sCarry);
+        fwd_tile<T, MODE, DH, L, NT, READOUT, true>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
     else
-        fwd_tile<T, MODE, DH, L, NT, READOUT, false>(p, tile, cb, sWP, sWE, sCarry);
+        fwd_tile<T, MODE, DH, L, NT, READOUT, false>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
 }
 
 template <typename T, int MODE, int DH>
