@@ -128,6 +128,25 @@ def bench_train(args, torch, binding, synth):
     out["fwd_gbs"] = fwd_bytes / (out["fwd_ms"] * 1e-3) / 1e9
     out["bwd_gbs"] = bwd_bytes / (out["bwd_ms"] * 1e-3) / 1e9
     out["fwd_tokens_per_s"] = B * T / (out["fwd_ms"] * 1e-3)
+    # this box's streaming reference on the same 4 GiB tensors: what plain elementwise kernels
+    # with the same read:write mixes reach (context for the roofline fraction; HBM speed
+    # differs from box to box by several percent)
+    def stream_gbs(fn, nbytes, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+
+    out["stream_reference"] = {
+        "copy_1r1w_GBs": stream_gbs(lambda: y.copy_(g["a"]), 2 * nelem * sb),
+        "addcmul_3r1w_GBs": stream_gbs(lambda: torch.addcmul(g["a"], g["v"], g["q"], out=y),
+                                       4 * nelem * sb),
+    }
     if not args.no_cpu_baseline:  # distinct batch rows for the oracle's timed sample
         out["inputs"] = {k: g[k][: args.cpu_threads].cpu() for k in ("a", "v", "q", "dy")}
     del g, y, eT
@@ -288,6 +307,7 @@ def main():
                               "traffic": measured_traffic(dom),
                               "algorithmic_bytes_per_launch": train[f"{dom}_bytes"],
                               "avg_launch_ms": round(train[f"{dom}_ms"], 4)}
+        result["stream_reference"] = train["stream_reference"]
         result["kernels"] = {
             "fwd": {"ms": round(train["fwd_ms"], 4), "GB_s": round(train["fwd_gbs"], 1),
                     "frac_hbm": round(train["fwd_gbs"] / HBM_PEAK_GBS, 4),

