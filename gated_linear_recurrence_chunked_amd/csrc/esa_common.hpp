@@ -77,9 +77,13 @@ struct Geom {
 };
 
 // Per-(dtype, Dh) launch configuration of the forward and backward scans.
+// The forward runs 512-thread workgroups (8 waves): at 64K context a tile is then 256 steps,
+// which halves the look-back words per byte of data against 256 threads and measured ~7 %
+// faster.  The backward holds more per thread (136 VGPRs, 3 waves per SIMD), so a 512-thread
+// workgroup would leave one workgroup per CU; it keeps 256 threads.
 template <typename T, int DH>
 struct FwdCfg {
-    static constexpr int NT = 256;
+    static constexpr int NT = 512;
     static constexpr int L = 4;
     using G = Geom<T, DH, L, NT>;
 };
