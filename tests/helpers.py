@@ -21,7 +21,10 @@ def f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def err(x, r) -> float:
+def err(x, r, floor: float = 0.0) -> float:
+    """The error above; `floor` (default 0) bounds the scale from below, for references whose
+    every element is numerically zero (e.g. the gate gradient of a saturated gate: exactly 0
+    in fp32, about 1e-44 in fp64)."""
     x = f64(x)
     r = f64(r)
     assert x.shape == r.shape, (x.shape, r.shape)
@@ -30,13 +33,13 @@ def err(x, r) -> float:
     if not np.all(np.isfinite(x)):
         return float("inf")
     rms = float(np.sqrt(np.mean(r * r)))
-    scale = np.maximum(np.abs(r), rms)
+    scale = np.maximum(np.maximum(np.abs(r), rms), floor)
     scale = np.where(scale > 0, scale, 1.0)
     return float(np.max(np.abs(x - r) / scale))
 
 
-def assert_close(name, x, r, dtype):
-    e = err(x, r)
+def assert_close(name, x, r, dtype, floor: float = 0.0):
+    e = err(x, r, floor)
     tol = TOL[dtype]
     assert e <= tol, f"{name}: err {e:.3e} > tol {tol:.0e}"
     return e

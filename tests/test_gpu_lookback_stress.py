@@ -1,0 +1,79 @@
+"""Look-back stress: long single chains of tiles and saturated gates, against the oracle.
+
+One channel block over T = 2^17 steps makes the longest chain the library builds (512 forward
+and 2048 backward tiles, each waiting on its predecessors' published pairs).  Saturated logits
+reach the special cases of page "Entangled State Attention v2.1"'s recurrence
+E_t = A_t E_{t-1} + B_t: a = +100 gives A = 1 exactly (a prefix sum over the whole sequence,
+the worst case for rounding), a = -100 gives A ~ 0 (every tile independent of its past).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_linear_recurrence_chunked_amd import binding, synth
+from helpers import assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_abort_clear():
+    torch.cuda.synchronize()
+    for ws in binding._workspaces.values():
+        assert int(ws[12:16].view(torch.int32).item()) == 0, "look-back wait timed out"
+
+
+@pytest.mark.parametrize("gate", ["random", "retain", "forget"])
+@pytest.mark.parametrize("dt,mode", [(torch.bfloat16, "direct"), (torch.float16, "controlled")])
+def test_long_single_chain(gate, dt, mode):
+    B, T, H, Dh = 1, 1 << 17, 1, 64
+    say(f"stress T={T} {gate} {dt} {mode}")
+    shp = (B, T, H, Dh)
+    a = synth.normal(shp, 901, 1.0, 2.0, dt)
+    if gate == "retain":
+        a = torch.full(shp, 100.0, dtype=dt)
+    elif gate == "forget":
+        a = torch.full(shp, -100.0, dtype=dt)
+    v = synth.normal(shp, 902, 0, 1, dt)
+    q = synth.normal(shp, 903, 0, 1, dt)
+    dy = synth.normal(shp, 904, 0, 1, dt)
+    e0 = synth.random_state(B, H, Dh, 905)
+    g = [t.to(DEV) for t in (a, v, q, dy)]
+    ge0 = e0.to(DEV)
+    y, eT, ck = binding.scan_fwd(g[0], g[1], g[2], ge0, mode=mode, return_ckpt=True)
+    da, dv, dq, de0 = binding.scan_bwd(g[0], g[1], g[2], g[3], ge0, None, ckpt=ck, mode=mode)
+    check_abort_clear()
+    m = 0 if mode == "direct" else 1
+    ry, reT = oracle.scan_fwd(a, v, q, e0, mode=m)
+    r = oracle.scan_bwd(a, v, q, dy, e0, None, mode=m)
+    assert_close("y", y, ry, dt)
+    assert_close("eT", eT, reT, dt)
+    for name, got, ref in zip(("d_logit", "d_value", "d_query", "d_init"), (da, dv, dq, de0), r):
+        # a saturated gate makes some outputs numerically zero (s (1 - s), and 1 - s or s
+        # itself, are 0 or ~1e-38 in fp32 but ~1e-44 in fp64): those are compared absolutely at
+        # the 1e-30 level; outputs of normal size are unaffected by the floor
+        floor = 1e-30 if gate != "random" else 0.0
+        assert_close(name, got, ref, dt, floor=floor)
+
+
+def test_repeated_runs_agree():
+    """Repeated runs on one workspace agree within the fp32 bar (the decoupled look-back may
+    associate the carries differently from run to run, so bits may differ)."""
+    say("repeat")
+    B, T, H, Dh = 4, 20000, 2, 64
+    x = {k: synth.normal((B, T, H, Dh), 910 + i, 0.0, 1.0, torch.float32).to(DEV)
+         for i, k in enumerate("avq")}
+    outs = [binding.scan_fwd(x["a"], x["v"], x["q"], mode="controlled") for _ in range(4)]
+    torch.cuda.synchronize()
+    for y, eT in outs[1:]:
+        assert_close("y", y, outs[0][0], torch.float32)
+        assert_close("eT", eT, outs[0][1], torch.float32)
+    check_abort_clear()
