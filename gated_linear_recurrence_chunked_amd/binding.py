@@ -90,8 +90,35 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _raw_stream(index: int) -> int:
+    """The current HIP stream of device `index` as an integer handle (torch's raw accessor,
+    without building a Python stream object: a decode step calls this once per token)."""
+    return torch._C._cuda_getCurrentRawStream(index)
+
+
 def _stream_handle(device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    return ctypes.c_void_p(_raw_stream(device.index))
+
+
+class _OnDevice:
+    """Makes `index` the current device for the call, and skips the switch when it already
+    is (the common case; a device switch costs more host time than a decode step's launch)."""
+    __slots__ = ("index", "prev")
+
+    def __init__(self, index: int):
+        self.index = index
+        self.prev = None
+
+    def __enter__(self):
+        cur = torch._C._cuda_getDevice()
+        if cur != self.index:
+            self.prev = cur
+            torch._C._cuda_setDevice(self.index)
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch._C._cuda_setDevice(self.prev)
+        return False
 
 
 def _mode(mode) -> int:
@@ -120,6 +147,15 @@ def _state(name, t, B, H, Dh, device):
     return t.contiguous()
 
 
+def _out(name, t, shape, dtype, device):
+    """A caller-provided output is written in place, so it must already be what the library
+    writes: contiguous, of the given shape, dtype and device (no copy is made)."""
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype
+            or t.device != device or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device}")
+
+
 def workspace_bytes(B, T, H, Dh, dtype) -> int:
     return int(load_library().esa_scan_workspace_bytes(B, T, H, Dh, DTYPES[dtype]))
 
@@ -135,7 +171,9 @@ def get_workspace(nbytes: int, device) -> torch.Tensor:
     zero-fills on allocation.  One workspace per stream: calls on one stream are ordered.
     """
     dev = torch.device(device)
-    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    key = (dev.index, _raw_stream(dev.index))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
@@ -154,15 +192,19 @@ def scan_fwd(a, v, q, init_state=None, mode="controlled", return_ckpt=False, fin
     init_state = _state("init_state", init_state, B, H, Dh, a.device)
     if y is None:
         y = torch.empty_like(a)
+    else:
+        _out("y", y, a.shape, a.dtype, a.device)
     if final_state is None:
         final_state = torch.empty((B, H, Dh), dtype=torch.float32, device=a.device)
+    else:
+        _out("final_state", final_state, (B, H, Dh), torch.float32, a.device)
     ckpt = None
     if return_ckpt:
         nck = max(1, ckpt_bytes(B, T, H, Dh) // 4)
         ckpt = torch.empty(nck, dtype=torch.float32, device=a.device)
     need = workspace_bytes(B, T, H, Dh, a.dtype)
     ws = workspace if workspace is not None else get_workspace(need, a.device)
-    with torch.cuda.device(a.device):
+    with _OnDevice(a.device.index):
         st = lib.esa_scan_fwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode), _ptr(a), _ptr(v), _ptr(q),
                               _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(ckpt), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream_handle(a.device))
@@ -193,7 +235,7 @@ def scan_bwd(a, v, q, dy, init_state=None, d_final_state=None, ckpt=None, mode="
     d_init = torch.empty((B, H, Dh), dtype=torch.float32, device=a.device)
     need = workspace_bytes(B, T, H, Dh, a.dtype)
     ws = workspace if workspace is not None else get_workspace(need, a.device)
-    with torch.cuda.device(a.device):
+    with _OnDevice(a.device.index):
         st = lib.esa_scan_bwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode), _ptr(a), _ptr(v), _ptr(q),
                               _ptr(init_state), _ptr(dy), _ptr(d_final_state), _ptr(ckpt),
                               _ptr(da), _ptr(dv), _ptr(dq), _ptr(d_init), _ptr(ws),
@@ -204,23 +246,31 @@ def scan_bwd(a, v, q, dy, init_state=None, d_final_state=None, ckpt=None, mode="
 
 def state_step(a, v, q, state, mode="controlled", y=None):
     """One-token update (esa_state_step): `state` (fp32 [B, H, Dh]) is updated in place."""
-    lib = load_library()
+    lib = _lib if _lib is not None else load_library()
     for name, t in (("gate_logit", a), ("value", v), ("query", q)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 3:
             raise ValueError(f"{name} must be a [B, H, Dh] CUDA (HIP) tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if v.shape != a.shape or q.shape != a.shape or v.dtype != a.dtype or q.dtype != a.dtype:
-        raise ValueError("gate_logit, value and query must share shape and dtype")
-    if a.dtype not in DTYPES:
+    dev = a.device
+    if (v.shape != a.shape or q.shape != a.shape or v.dtype != a.dtype or q.dtype != a.dtype
+            or v.device != dev or q.device != dev):
+        raise ValueError("gate_logit, value and query must share shape, dtype and device")
+    code = DTYPES.get(a.dtype)
+    if code is None:
         raise TypeError(f"dtype {a.dtype} not supported")
     B, H, Dh = a.shape
-    if state.dtype != torch.float32 or tuple(state.shape) != (B, H, Dh) or not state.is_contiguous():
-        raise ValueError("state must be a contiguous fp32 [B, H, Dh] tensor")
+    if (not isinstance(state, torch.Tensor) or state.dtype != torch.float32
+            or state.shape != a.shape or state.device != dev or not state.is_contiguous()):
+        raise ValueError("state must be a contiguous fp32 [B, H, Dh] tensor on the inputs' device")
     if y is None:
         y = torch.empty_like(a)
-    with torch.cuda.device(a.device):
-        st = lib.esa_state_step(B, H, Dh, DTYPES[a.dtype], _mode(mode), _ptr(a), _ptr(v), _ptr(q),
-                                _ptr(state), _ptr(y), _stream_handle(a.device))
+    elif (not isinstance(y, torch.Tensor) or y.dtype != a.dtype or y.shape != a.shape
+          or y.device != dev or not y.is_contiguous()):
+        raise ValueError("y must be a contiguous [B, H, Dh] tensor of the inputs' dtype and device")
+    index = dev.index
+    with _OnDevice(index):
+        st = lib.esa_state_step(B, H, Dh, code, _mode(mode), a.data_ptr(), v.data_ptr(),
+                                q.data_ptr(), state.data_ptr(), y.data_ptr(), _raw_stream(index))
     _check(st, "esa_state_step")
     return y

@@ -171,6 +171,34 @@ def test_in_place_final_state():
     assert_close("state", st, reT, torch.float16)
 
 
+def test_binding_rejects_mismatched_outputs():
+    """Caller-provided outputs are written in place: a wrong shape, dtype or layout is an
+    error, never a silent write past the tensor."""
+    say("binding output validation")
+    B, T, H, Dh = 2, 64, 2, 64
+    x = {k: t.to(DEV) for k, t in inputs_cpu(B, T, H, Dh, torch.float16, seed=77).items()}
+    bad_y = [torch.empty(B, T, H, Dh, device=DEV, dtype=torch.float32),
+             torch.empty(B, T - 1, H, Dh, device=DEV, dtype=torch.float16),
+             torch.empty(B, H, T, Dh, device=DEV, dtype=torch.float16).transpose(1, 2)]
+    for y in bad_y:
+        with pytest.raises(ValueError):
+            binding.scan_fwd(x["a"], x["v"], x["q"], y=y)
+    for eT in (torch.empty(B, H, Dh, device=DEV, dtype=torch.float16),
+               torch.empty(B, H, Dh + 1, device=DEV)[..., :Dh]):
+        with pytest.raises(ValueError):
+            binding.scan_fwd(x["a"], x["v"], x["q"], final_state=eT)
+    a1, v1, q1 = (x[k][:, 0].contiguous() for k in "avq")
+    st = torch.zeros(B, H, Dh, device=DEV)
+    for y in (torch.empty(B, H, Dh, device=DEV), torch.empty(B, H, 2 * Dh, device=DEV,
+                                                               dtype=torch.float16)[..., ::2]):
+        with pytest.raises(ValueError):
+            binding.state_step(a1, v1, q1, st, y=y)
+    with pytest.raises(ValueError):
+        binding.state_step(a1, v1, q1, st.to(torch.float16))
+    with pytest.raises(ValueError):
+        binding.state_step(a1, v1, q1, st.cpu())
+
+
 def test_saturated_gates_reach_special_cases():
     """a = +100 gives A = 1 exactly (a prefix sum over t); a = -100 gives A ~ 0 (E = v)."""
     say("saturated gates")
