@@ -9,8 +9,8 @@ kernels.  When the library is missing, every call raises; there is no fallback p
                                   ckpt=None, mode="controlled")
     y = state_step(a, v, q, state, mode="controlled")        # state: fp32, updated in place
 
-Sequence tensors are [B, T, H, Dh] (fp32, fp16 or bf16, one dtype per call); states are
-fp32 [B, H, Dh].
+Sequence tensors are [B, T, H, Dh] (fp32, fp16, bf16, or the OCP 8-bit formats
+float8_e4m3fn / float8_e5m2; one dtype per call); states are fp32 [B, H, Dh].
 """
 from __future__ import annotations
 
@@ -26,7 +26,8 @@ LIB_NAME = "libesa.so"
 ESA_OK = 0
 STATUS_NAMES = {0: "ESA_OK", 1: "ESA_ERR_INVALID_ARG", 2: "ESA_ERR_UNSUPPORTED",
                 3: "ESA_ERR_WORKSPACE", 4: "ESA_ERR_HIP"}
-DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4m3fn: 3,
+          torch.float8_e5m2: 4}
 MODES = {"direct": 0, "controlled": 1}
 
 # every function include/esa.h declares: name -> (restype, argtypes)

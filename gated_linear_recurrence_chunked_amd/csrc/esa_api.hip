@@ -44,7 +44,18 @@ TileShape tile_shape(int dtype, int64_t Dh) {
     switch (dtype) {
         case ESA_F32: return tile_shape_dh<float>(Dh);
         case ESA_F16: return tile_shape_dh<_Float16>(Dh);
-        default: return tile_shape_dh<__bf16>(Dh);
+        case ESA_BF16: return tile_shape_dh<__bf16>(Dh);
+        case ESA_F8E4M3: return tile_shape_dh<f8e4m3>(Dh);
+        default: return tile_shape_dh<f8e5m2>(Dh);
+    }
+}
+
+int64_t storage_bytes(int dtype) {
+    switch (dtype) {
+        case ESA_F32: return 4;
+        case ESA_F16:
+        case ESA_BF16: return 2;
+        default: return 1;
     }
 }
 
@@ -57,7 +68,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int check_sizes(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode, Problem* pr) {
-    if (dtype < ESA_F32 || dtype > ESA_BF16 || mode < ESA_DIRECT || mode > ESA_CONTROLLED)
+    if (dtype < ESA_F32 || dtype > ESA_F8E5M2 || mode < ESA_DIRECT || mode > ESA_CONTROLLED)
         return ESA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || Dh < 1 || T < 0) return ESA_ERR_INVALID_ARG;
     if (!supported_dh(Dh)) return ESA_ERR_UNSUPPORTED;
@@ -67,7 +78,7 @@ int check_sizes(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode
     pr->Dh = Dh;
     pr->dtype = dtype;
     pr->mode = mode;
-    pr->esize = dtype == ESA_F32 ? 4 : 2;
+    pr->esize = storage_bytes(dtype);
     int64_t bytes;
     if (!mul64(H, Dh, &pr->C) || !mul64(B, pr->C, &pr->nLanes) || !mul64(pr->nLanes, T, &pr->nElem) ||
         !mul64(pr->nElem, 4, &bytes) || !mul64(pr->nLanes, 16, &bytes))
@@ -136,7 +147,11 @@ bool any_overlap(const Range* in, int nin, const Range* out, int nout) {
             case ESA_F16 * 2 + 0: return KIND##_dh<_Float16, 0>(Dh, params, stream);         \
             case ESA_F16 * 2 + 1: return KIND##_dh<_Float16, 1>(Dh, params, stream);         \
             case ESA_BF16 * 2 + 0: return KIND##_dh<__bf16, 0>(Dh, params, stream);          \
-            default: return KIND##_dh<__bf16, 1>(Dh, params, stream);                        \
+            case ESA_BF16 * 2 + 1: return KIND##_dh<__bf16, 1>(Dh, params, stream);          \
+            case ESA_F8E4M3 * 2 + 0: return KIND##_dh<f8e4m3, 0>(Dh, params, stream);        \
+            case ESA_F8E4M3 * 2 + 1: return KIND##_dh<f8e4m3, 1>(Dh, params, stream);        \
+            case ESA_F8E5M2 * 2 + 0: return KIND##_dh<f8e5m2, 0>(Dh, params, stream);        \
+            default: return KIND##_dh<f8e5m2, 1>(Dh, params, stream);                        \
         }                                                                                     \
     }()
 

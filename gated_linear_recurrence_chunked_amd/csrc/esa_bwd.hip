@@ -200,31 +200,28 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     __syncthreads();
     slots_phase_b<G, true>(sP, sE, sWP, sWE, xp, xe);
 
-    // ---- reverse look-back across tiles, by wave 0 (lane = channel) ----
-    if (w == 0) {
-#pragma unroll
-        for (int k = 0; k < G::CPL; ++k) {
-            const int ch = (tid % kWave) + k * kWave;
-            float tp, te;
-            tile_total<G, true>(sWP, sWE, ch, tp, te);
-            const int64_t gl = (int64_t)cb * CB + ch;
-            float carry = 0.0f;
-            if (FULL || gl < p.nLanes) {
-                uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
-                if (tile == p.nTiles - 1) {
-                    carry = p.dET ? p.dET[gl] : 0.0f;
-                } else {
-                    publish(X, tagAgg, te);
-                    publish(p.flagY + (int64_t)tile * p.nLanes + gl, tagAgg, tp);
-                    carry = look_back(p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc,
-                                      p.hdr);
-                }
-                const float lam_out = te + tp * carry;
-                publish(X, tagInc, lam_out);
-                if (tile == 0 && p.de0) p.de0[gl] = lam_out;
+    // ---- reverse look-back across tiles, wave k for channels 64k.. (lane = channel) ----
+    if (w < G::CPL) {
+        const int ch = (tid % kWave) + w * kWave;
+        float tp, te;
+        tile_total<G, true>(sWP, sWE, ch, tp, te);
+        const int64_t gl = (int64_t)cb * CB + ch;
+        float carry = 0.0f;
+        if (FULL || gl < p.nLanes) {
+            uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
+            if (tile == p.nTiles - 1) {
+                carry = p.dET ? p.dET[gl] : 0.0f;
+            } else {
+                publish(X, tagAgg, te);
+                publish(p.flagY + (int64_t)tile * p.nLanes + gl, tagAgg, tp);
+                carry = look_back(p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc,
+                                  p.hdr);
             }
-            sCarry[ch] = carry;
+            const float lam_out = te + tp * carry;
+            publish(X, tagInc, lam_out);
+            if (tile == 0 && p.de0) p.de0[gl] = lam_out;
         }
+        sCarry[ch] = carry;
     }
     __syncthreads();
     read_exclusive<G>(sP, sE, XP, XE);
@@ -293,5 +290,9 @@ ESA_INST_BWD_D(_Float16, 0)
 ESA_INST_BWD_D(_Float16, 1)
 ESA_INST_BWD_D(__bf16, 0)
 ESA_INST_BWD_D(__bf16, 1)
+ESA_INST_BWD_D(f8e4m3, 0)
+ESA_INST_BWD_D(f8e4m3, 1)
+ESA_INST_BWD_D(f8e5m2, 0)
+ESA_INST_BWD_D(f8e5m2, 1)
 
 }  // namespace esa

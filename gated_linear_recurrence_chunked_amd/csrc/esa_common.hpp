@@ -8,7 +8,8 @@
 // "[ ARCHITECTURE ]", associative composition):
 //
 //   lanes    a thread owns VEC channels (16 bytes of storage) of one (b, t); CB channels
-//            (whole heads, at least 64) form a channel block, NCL = CB / VEC threads wide.
+//            (whole heads, at least 64 channels and 128 bytes) form a channel block,
+//            NCL = CB / VEC threads wide.
 //   tile     a workgroup owns one channel block over TT = S * L time steps: S time slots
 //            of L consecutive steps, one slot per row of NCL threads.
 //   level 1  each thread folds its L steps in registers into one pair per channel.
@@ -58,33 +59,61 @@ template <>
 struct Storage<__bf16> {
     static constexpr int VEC = 8;
 };
+// One-byte floating-point storage in the two OCP 8-bit formats: E4M3 (4 exponent bits, bias
+// 7, no infinities, max 448) and E5M2 (5 exponent bits, bias 15, IEEE-style infinities, max
+// 57344).  The kernels decode them exactly to fp32 and round results back to nearest even
+// with the gfx950 conversion instructions.
+struct f8e4m3 {
+    uint8_t bits;
+};
+struct f8e5m2 {
+    uint8_t bits;
+};
+template <>
+struct Storage<f8e4m3> {
+    static constexpr int VEC = 16;
+};
+template <>
+struct Storage<f8e5m2> {
+    static constexpr int VEC = 16;
+};
 
-// Tile geometry of a scan kernel instance.
+// Tile geometry of a scan kernel instance.  A channel block spans at least 64 channels and at
+// least 128 bytes of each time row: with one-byte storage a 64-channel row piece is 64 bytes,
+// and rows read in 64-byte pieces stream at about two thirds of the rate of 128-byte pieces.
 template <typename T, int DH, int L, int NT>
 struct Geom {
     static constexpr int VEC = Storage<T>::VEC;
-    static constexpr int CB = DH > 64 ? DH : 64;  // channels per block (whole heads)
+    static constexpr int CBMIN = 128 / (int)sizeof(T) > 64 ? 128 / (int)sizeof(T) : 64;
+    static constexpr int CB = DH > CBMIN ? DH : CBMIN;  // channels per block (whole heads)
     static constexpr int NCL = CB / VEC;          // threads across one time row
     static constexpr int S = NT / NCL;            // time slots per tile
     static constexpr int TT = S * L;              // time steps per tile
     static constexpr int HL = DH / VEC;           // threads per head
-    static constexpr int CPL = CB / kWave;        // channels per lane of the look-back wave
+    static constexpr int CPL = CB / kWave;        // channels per lane in the slot scans, and
+                                                  // look-back waves (one per 64 channels)
     static constexpr int NW = NT / kWave;         // waves per workgroup
     static constexpr int SPW = kWave / NCL;       // time slots per wave
     static_assert(CB % VEC == 0 && NT % NCL == 0 && S >= 1, "bad tile geometry");
     static_assert(kWave % NCL == 0 && CB % kWave == 0, "a wave holds whole rows of a block");
     static_assert(HL >= 1 && (HL & (HL - 1)) == 0 && HL <= kWave, "head must be 2^k lanes");
+    static_assert(NW >= CPL, "one look-back wave per 64 channels of the block");
 };
 
 // Per-(dtype, Dh) launch configuration of the forward and backward scans.
 // The forward runs 512-thread workgroups (8 waves): at 64K context a tile is then 256 steps,
 // which halves the look-back words per byte of data against 256 threads and measured ~7 %
-// faster.  The backward holds more per thread (136 VGPRs, 3 waves per SIMD), so a 512-thread
+// faster.  The backward holds more per thread (231 VGPRs, 2 waves per SIMD), so a 512-thread
 // workgroup would leave one workgroup per CU; it keeps 256 threads.
+// A thread holds at most 32 elements per step group: four steps of 8 channels, or two steps
+// of 16 channels for one-byte storage (more would spill the backward's registers).  The
+// one-byte forward needs 132 VGPRs, which fit three waves per SIMD: 256-thread workgroups
+// then run three to a CU, measured 1.45x faster at 64K context than one 512-thread
+// workgroup per CU.
 template <typename T, int DH>
 struct FwdCfg {
-    static constexpr int NT = 512;
-    static constexpr int L = 4;
+    static constexpr int NT = Storage<T>::VEC == 16 ? 256 : 512;
+    static constexpr int L = 32 / Storage<T>::VEC < 4 ? 32 / Storage<T>::VEC : 4;
     using G = Geom<T, DH, L, NT>;
 };
 template <typename T, int DH>
@@ -94,7 +123,8 @@ struct BwdCfg {
     // four steps per thread (at least 64 steps per tile): deeper tiles halve the look-back
     // words against two steps per thread and measured ~3 % faster at 64K context, although
     // the 231 VGPRs then allow two waves per SIMD rather than three
-    static constexpr int L = 4 * S0 >= kCkptChunk ? 4 : kCkptChunk / S0;
+    static constexpr int LR = 32 / Storage<T>::VEC < 4 ? 32 / Storage<T>::VEC : 4;
+    static constexpr int L = LR * S0 >= kCkptChunk ? LR : kCkptChunk / S0;
     using G = Geom<T, DH, L, NT>;
     // the backward tile must start on a checkpoint boundary
     static_assert(G::TT % kCkptChunk == 0, "backward tile must be a multiple of 64 steps");
@@ -212,6 +242,37 @@ __device__ __forceinline__ void unpack<__bf16>(const uint4& r, float* out) {
     }
 }
 
+// One-byte formats: each 32-bit word holds four values, byte k = element k; the packed
+// conversions take or fill the low (false) or high (true) 16-bit half of a word.
+typedef float f2_t __attribute__((ext_vector_type(2)));
+template <bool E5M2>
+__device__ __forceinline__ void unpack_f8(const uint4& r, float* out) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        f2_t lo, hi;
+        if constexpr (E5M2) {
+            lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w[k], false);
+            hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w[k], true);
+        } else {
+            lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+            hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+        }
+        out[4 * k] = lo.x;
+        out[4 * k + 1] = lo.y;
+        out[4 * k + 2] = hi.x;
+        out[4 * k + 3] = hi.y;
+    }
+}
+template <>
+__device__ __forceinline__ void unpack<f8e4m3>(const uint4& r, float* out) {
+    unpack_f8<false>(r, out);
+}
+template <>
+__device__ __forceinline__ void unpack<f8e5m2>(const uint4& r, float* out) {
+    unpack_f8<true>(r, out);
+}
+
 // VEC fp32 values -> 16 bytes of storage (round to nearest even).
 template <typename T>
 __device__ __forceinline__ uint4 pack(const float* x);
@@ -239,6 +300,34 @@ __device__ __forceinline__ uint4 pack<__bf16>(const float* x) {
         w[k] = __builtin_bit_cast(uint32_t, h);
     }
     return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Out-of-range values follow the formats' own conversion: NaN for E4M3 beyond 464 in
+// magnitude, infinity for E5M2 beyond 61440.
+template <bool E5M2>
+__device__ __forceinline__ uint4 pack_f8(const float* x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int v;
+        if constexpr (E5M2) {
+            v = __builtin_amdgcn_cvt_pk_bf8_f32(x[4 * k], x[4 * k + 1], 0, false);
+            v = __builtin_amdgcn_cvt_pk_bf8_f32(x[4 * k + 2], x[4 * k + 3], v, true);
+        } else {
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k], x[4 * k + 1], 0, false);
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k + 2], x[4 * k + 3], v, true);
+        }
+        w[k] = (uint32_t)v;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+template <>
+__device__ __forceinline__ uint4 pack<f8e4m3>(const float* x) {
+    return pack_f8<false>(x);
+}
+template <>
+__device__ __forceinline__ uint4 pack<f8e5m2>(const float* x) {
+    return pack_f8<true>(x);
 }
 
 // Raw buffer access for tiles that lie inside one batch row: a workgroup-uniform resource

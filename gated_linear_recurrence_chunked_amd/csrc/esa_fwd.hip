@@ -104,29 +104,26 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
     __syncthreads();
     slots_phase_b<G, false>(sP, sE, sWP, sWE, xp, xe);
 
-    // ---- level 3: decoupled look-back across tiles, by wave 0 (lane = channel) ----
-    if (w == 0) {
-#pragma unroll
-        for (int k = 0; k < G::CPL; ++k) {
-            const int ch = (tid % kWave) + k * kWave;
-            float tp, te;
-            tile_total<G, false>(sWP, sWE, ch, tp, te);
-            const int64_t gl = (int64_t)cb * CB + ch;
-            float carry = 0.0f;
-            if (FULL || gl < p.nLanes) {
-                uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
-                if (tile == 0) {
-                    carry = p.e0 ? p.e0[gl] : 0.0f;
-                } else {
-                    publish(X, tagAgg, te);
-                    publish(p.flagY + (int64_t)tile * p.nLanes + gl, tagAgg, tp);
-                    carry = look_back(p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg, tagInc,
-                                      p.hdr);
-                }
-                publish(X, tagInc, te + tp * carry);
+    // ---- level 3: decoupled look-back across tiles, wave k for channels 64k.. (lane = channel) ----
+    if (w < G::CPL) {
+        const int ch = (tid % kWave) + w * kWave;
+        float tp, te;
+        tile_total<G, false>(sWP, sWE, ch, tp, te);
+        const int64_t gl = (int64_t)cb * CB + ch;
+        float carry = 0.0f;
+        if (FULL || gl < p.nLanes) {
+            uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
+            if (tile == 0) {
+                carry = p.e0 ? p.e0[gl] : 0.0f;
+            } else {
+                publish(X, tagAgg, te);
+                publish(p.flagY + (int64_t)tile * p.nLanes + gl, tagAgg, tp);
+                carry = look_back(p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg, tagInc,
+                                  p.hdr);
             }
-            sCarry[ch] = carry;
+            publish(X, tagInc, te + tp * carry);
         }
+        sCarry[ch] = carry;
     }
     __syncthreads();
 
@@ -217,5 +214,9 @@ ESA_INST_FWD_D(_Float16, 0)
 ESA_INST_FWD_D(_Float16, 1)
 ESA_INST_FWD_D(__bf16, 0)
 ESA_INST_FWD_D(__bf16, 1)
+ESA_INST_FWD_D(f8e4m3, 0)
+ESA_INST_FWD_D(f8e4m3, 1)
+ESA_INST_FWD_D(f8e5m2, 0)
+ESA_INST_FWD_D(f8e5m2, 1)
 
 }  // namespace esa

@@ -81,6 +81,10 @@ ESA_INST_STEP_D(_Float16, 0)
 ESA_INST_STEP_D(_Float16, 1)
 ESA_INST_STEP_D(__bf16, 0)
 ESA_INST_STEP_D(__bf16, 1)
+ESA_INST_STEP_D(f8e4m3, 0)
+ESA_INST_STEP_D(f8e4m3, 1)
+ESA_INST_STEP_D(f8e5m2, 0)
+ESA_INST_STEP_D(f8e5m2, 1)
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* dst, int64_t nwords, uint8_t* tail,
                                                         int64_t ntail) {

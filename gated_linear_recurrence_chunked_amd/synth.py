@@ -17,6 +17,9 @@ Workloads (all sequences are [B, T, H, Dh], Dh fastest; states [B, H, Dh] fp32):
   decode_f16        B=256, T in {512, 1024, 4096, 8192}, H=8, Dh=64, fp16 controlled, all
                     N(0, 1), then 1024 one-token steps with fresh N(0, 1) inputs
                     (prompt lengths of "[ GENERATION / MEMORY ]" on the same page)
+  long64k_f8e4m3    the long64k_f16 shapes and draws, stored in the OCP E4M3 8-bit format
+                    (the experimental fp8 precision mode of page "Entangled State Attention
+                    v2.1", section "3. Precision")
 
 The second parameter of N(mu, s) is the standard deviation.  Seed of tensor k of workload
 number w is 1000 * w + k with k = 0 (a), 1 (v), 2 (q), 3 (dy), 4 + step (decode draws; the
@@ -52,9 +55,12 @@ WORKLOADS = {
     "train8k_bf16": Workload("train8k_bf16", 4, 16, 8192, 8, 64, "bf16", "direct", 1.0, 1.0),
     "decode_f16": Workload("decode_f16", 5, 256, 512, 8, 64, "f16", "controlled", 0.0, 1.0,
                            prompts=(512, 1024, 4096, 8192), steps=1024),
+    "long64k_f8e4m3": Workload("long64k_f8e4m3", 6, 64, 65536, 8, 64, "f8e4m3", "controlled",
+                               2.0, 1.0),
 }
 
-TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+                "f8e4m3": torch.float8_e4m3fn, "f8e5m2": torch.float8_e5m2}
 
 
 def torch_dtype(name: str) -> torch.dtype:

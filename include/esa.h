@@ -18,7 +18,9 @@
  *
  * Layout.  Sequence tensors are contiguous [B, T, H, Dh] with Dh fastest, in the storage
  * dtype.  States are contiguous [B, H, Dh] and always fp32.  All arithmetic is fp32 with
- * fp32 accumulation; outputs in a 16-bit dtype are rounded to nearest even.
+ * fp32 accumulation; outputs in a 16- or 8-bit dtype are rounded to nearest even.  An 8-bit
+ * output beyond its format's range becomes what the format's conversion gives: NaN for E4M3
+ * (magnitude at least 464), infinity for E5M2 (at least 61440).
  *
  * Ownership and execution.  The caller owns every buffer (device memory).  The library
  * never allocates, frees or synchronises; each call validates its arguments on the host,
@@ -48,7 +50,8 @@
 extern "C" {
 #endif
 
-#define ESA_ABI_VERSION 1
+/* 1: fp32 / fp16 / bf16 storage.  2: adds the fp8 storage dtypes ESA_F8E4M3, ESA_F8E5M2. */
+#define ESA_ABI_VERSION 2
 
 /* Checkpoint granularity: the forward can store the fp32 state at every 64th step. */
 #define ESA_CKPT_CHUNK 64
@@ -62,8 +65,17 @@ typedef enum {
 } esa_status;
 
 /* Storage dtype of the sequence tensors (precision modes of page "Entangled State
- * Attention v2.1", section "3. Precision": fp16 default, bf16, fp32). */
-typedef enum { ESA_F32 = 0, ESA_F16 = 1, ESA_BF16 = 2 } esa_dtype;
+ * Attention v2.1", section "3. Precision": fp16 default, bf16, fp32, and fp8, which that
+ * section calls experimental).  The fp8 dtypes are the OCP 8-bit formats: E4M3 (no
+ * infinities, largest finite 448) and E5M2 (largest finite 57344).  One dtype serves every
+ * sequence tensor of a call; arithmetic and states stay fp32 whatever the storage. */
+typedef enum {
+    ESA_F32 = 0,
+    ESA_F16 = 1,
+    ESA_BF16 = 2,
+    ESA_F8E4M3 = 3,
+    ESA_F8E5M2 = 4
+} esa_dtype;
 
 /* Recurrence form (page "entangled-state-attention 0.1.0", "Direct vs controlled mode"). */
 typedef enum { ESA_DIRECT = 0, ESA_CONTROLLED = 1 } esa_mode;

@@ -7,12 +7,17 @@ The error of a result x against the oracle's r is
 an elementwise relative error wherever |r_i| >= rms(r), and an absolute error scaled by
 rms(r) below it.  A pure elementwise ratio is undefined where r_i = 0 and unbounded near
 it, and the states and gradients here are signed sums that cancel.  The bar is 1e-5 for
-fp32 inputs and 5e-3 for fp16 / bf16 inputs.
+fp32 inputs, 5e-3 for fp16 / bf16 inputs and the format's rounding bound for fp8 inputs.
 """
 import numpy as np
 import torch
 
-TOL = {torch.float32: 1e-5, torch.float16: 5e-3, torch.bfloat16: 5e-3}
+# fp8 storage: the outputs are rounded once to the 8-bit format, whose relative rounding
+# error is at most 2^-4 (E4M3, 3 stored mantissa bits) or 2^-3 (E5M2, 2 bits) in the normal
+# range; below it the rounding is absolute (at most 2^-10 for E4M3, 2^-17 for E5M2) and the
+# metric scales it by rms(r).  The fp32 arithmetic adds ~1e-6 on top.
+TOL = {torch.float32: 1e-5, torch.float16: 5e-3, torch.bfloat16: 5e-3,
+       torch.float8_e4m3fn: 2.0 ** -4 + 1e-4, torch.float8_e5m2: 2.0 ** -3 + 1e-4}
 
 
 def f64(x):
@@ -41,5 +46,6 @@ def err(x, r, floor: float = 0.0) -> float:
 def assert_close(name, x, r, dtype, floor: float = 0.0):
     e = err(x, r, floor)
     tol = TOL[dtype]
+    print(f"  {name}: err {e:.3e} (bar {tol:.0e})", flush=True)
     assert e <= tol, f"{name}: err {e:.3e} > tol {tol:.0e}"
     return e

@@ -40,8 +40,14 @@ def test_every_declared_symbol_is_exported(lib):
         assert n in binding.SIGNATURES, n
 
 
+def header_abi_version() -> int:
+    import re
+    text = open(os.path.join(ROOT, "include", "esa.h")).read()
+    return int(re.search(r"#define ESA_ABI_VERSION (\d+)", text).group(1))
+
+
 def test_version_and_status_strings(lib):
-    assert lib.esa_abi_version() == 1
+    assert lib.esa_abi_version() == header_abi_version() == 2
     for s in range(5):
         assert lib.esa_status_string(s).decode().startswith(
             ["ESA_OK", "ESA_ERR_INVALID_ARG", "ESA_ERR_UNSUPPORTED", "ESA_ERR_WORKSPACE",
@@ -57,6 +63,11 @@ def test_workspace_and_ckpt_sizes(lib):
     assert ws(1, 10, 2, 48, 1) == 0  # unsupported Dh
     assert ws(0, 10, 2, 16, 1) == 0
     assert ws(1, 10, 2, 16, 7) == 0
+    assert ws(1, 10, 2, 16, 5) == 0
+    # fp8 storage (3 = E4M3, 4 = E5M2): 128-channel blocks, shorter tiles, so more
+    # look-back words than 16-bit storage at the same shape
+    assert ws(1, 256, 2, 16, 3) > 256 and ws(1, 256, 2, 16, 4) == ws(1, 256, 2, 16, 3)
+    assert ws(64, 65536, 8, 64, 3) > ws(64, 65536, 8, 64, 1)
     ck = lib.esa_scan_ckpt_bytes
     assert ck(2, 64, 3, 16) == 2 * 1 * 3 * 16 * 4
     assert ck(2, 65, 3, 16) == 2 * 2 * 3 * 16 * 4
@@ -88,7 +99,8 @@ def test_fwd_validation(lib):
     assert fwd(lib, y=None) == INVALID
     assert fwd(lib, B=0) == INVALID
     assert fwd(lib, T=-1) == INVALID
-    assert fwd(lib, dt=3) == INVALID
+    assert fwd(lib, dt=5) == INVALID
+    assert fwd(lib, dt=-1) == INVALID
     assert fwd(lib, mode=2) == INVALID
     assert fwd(lib, Dh=48) == UNSUPPORTED
     assert fwd(lib, Dh=256) == UNSUPPORTED

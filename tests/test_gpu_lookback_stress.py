@@ -64,6 +64,34 @@ def test_long_single_chain(gate, dt, mode):
         assert_close(name, got, ref, dt, floor=floor)
 
 
+@pytest.mark.parametrize("dt,mode", [(torch.float8_e4m3fn, "controlled"),
+                                     (torch.float8_e5m2, "direct")])
+def test_long_single_chain_fp8(dt, mode):
+    """fp8 storage: 128-channel blocks and the shortest tiles (2048 forward and 2048 backward
+    tiles in the chain).  Random gates only: a saturated gate makes the direct-mode sums and
+    their gradients outgrow the 8-bit range."""
+    B, T, H, Dh = 1, 1 << 17, 2, 64
+    say(f"stress fp8 T={T} {dt} {mode}")
+    shp = (B, T, H, Dh)
+    a = synth.normal(shp, 911, 1.0, 2.0, dt)
+    v = synth.normal(shp, 912, 0, 1, dt)
+    q = synth.normal(shp, 913, 0, 1, dt)
+    dy = synth.normal(shp, 914, 0, 1, dt)
+    e0 = synth.random_state(B, H, Dh, 915)
+    g = [t.to(DEV) for t in (a, v, q, dy)]
+    ge0 = e0.to(DEV)
+    y, eT, ck = binding.scan_fwd(g[0], g[1], g[2], ge0, mode=mode, return_ckpt=True)
+    da, dv, dq, de0 = binding.scan_bwd(g[0], g[1], g[2], g[3], ge0, None, ckpt=ck, mode=mode)
+    check_abort_clear()
+    m = 0 if mode == "direct" else 1
+    ry, reT = oracle.scan_fwd(a, v, q, e0, mode=m)
+    r = oracle.scan_bwd(a, v, q, dy, e0, None, mode=m)
+    assert_close("y", y, ry, dt)
+    assert_close("eT", eT, reT, torch.float16)
+    for name, got, ref in zip(("d_logit", "d_value", "d_query", "d_init"), (da, dv, dq, de0), r):
+        assert_close(name, got, ref, torch.float16 if name == "d_init" else dt)
+
+
 def test_repeated_runs_agree():
     """Repeated runs on one workspace agree within the fp32 bar (the decoupled look-back may
     associate the carries differently from run to run, so bits may differ)."""
