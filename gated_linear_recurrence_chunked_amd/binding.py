@@ -9,6 +9,13 @@ kernels.  When the library is missing, every call raises; there is no fallback p
                                   ckpt=None, mode="controlled")
     y = state_step(a, v, q, state, mode="controlled")        # state: fp32, updated in place
 
+Sequence segments (the scan over T cut into consecutive pieces, e.g. one per device):
+
+    seg_state, seg_prod = segment_fwd(a_k, v_k)              # per segment, from a zero state
+    carry, final = segment_compose(P_all, E_all, init_state)  # [nseg, B, H, Dh] stacks
+    seg_d_init = segment_bwd(a_k, v_k, q_k, dy_k, carry[k], ckpt_k)
+    dcarry, d_init = segment_compose(P_all, D_all, d_final_state, reverse=True)
+
 Sequence tensors are [B, T, H, Dh] (fp32, fp16, bf16, or the OCP 8-bit formats
 float8_e4m3fn / float8_e5m2; one dtype per call); states are fp32 [B, H, Dh].
 """
@@ -45,6 +52,10 @@ SIGNATURES = {
     "esa_scan_bwd": (_C, [_I, _I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                           _P, _P, _Z, _P]),
     "esa_state_step": (_C, [_I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _P]),
+    "esa_scan_segment_fwd": (_C, [_I, _I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _Z, _P]),
+    "esa_scan_segment_bwd": (_C, [_I, _I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+                                  _P]),
+    "esa_segment_compose": (_C, [_I, _I, _C, _P, _P, _P, _P, _P, _P]),
 }
 
 _lock = threading.Lock()
@@ -275,3 +286,74 @@ def state_step(a, v, q, state, mode="controlled", y=None):
                                 q.data_ptr(), state.data_ptr(), y.data_ptr(), _raw_stream(index))
     _check(st, "esa_state_step")
     return y
+
+
+def segment_fwd(a, v, mode="controlled", workspace=None):
+    """Aggregate of one sequence segment from a zero state (esa_scan_segment_fwd): returns
+    (seg_state, seg_gate_prod), fp32 [B, H, Dh] each."""
+    lib = load_library()
+    a = _seq("gate_logit", a)
+    v = _seq("value", v, a)
+    B, T, H, Dh = a.shape
+    seg_state = torch.empty((B, H, Dh), dtype=torch.float32, device=a.device)
+    seg_prod = torch.empty_like(seg_state)
+    need = workspace_bytes(B, T, H, Dh, a.dtype)
+    ws = workspace if workspace is not None else get_workspace(need, a.device)
+    with _OnDevice(a.device.index):
+        st = lib.esa_scan_segment_fwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode), _ptr(a), _ptr(v),
+                                      _ptr(seg_state), _ptr(seg_prod), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream_handle(a.device))
+    _check(st, "esa_scan_segment_fwd")
+    return seg_state, seg_prod
+
+
+def segment_bwd(a, v, q, dy, init_state=None, ckpt=None, mode="controlled", workspace=None):
+    """Gradient reaching a segment's initial state with none arriving at its end
+    (esa_scan_segment_bwd): fp32 [B, H, Dh]."""
+    lib = load_library()
+    a = _seq("gate_logit", a)
+    v = _seq("value", v, a)
+    q = _seq("query", q, a)
+    dy = _seq("dy", dy, a)
+    B, T, H, Dh = a.shape
+    init_state = _state("init_state", init_state, B, H, Dh, a.device)
+    if ckpt is not None:
+        if ckpt.dtype != torch.float32 or ckpt.numel() * 4 < ckpt_bytes(B, T, H, Dh):
+            raise ValueError("ckpt must be the fp32 checkpoint of scan_fwd(return_ckpt=True)")
+        ckpt = ckpt.contiguous()
+    seg_d_init = torch.empty((B, H, Dh), dtype=torch.float32, device=a.device)
+    need = workspace_bytes(B, T, H, Dh, a.dtype)
+    ws = workspace if workspace is not None else get_workspace(need, a.device)
+    with _OnDevice(a.device.index):
+        st = lib.esa_scan_segment_bwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode), _ptr(a), _ptr(v),
+                                      _ptr(q), _ptr(init_state), _ptr(dy), _ptr(ckpt),
+                                      _ptr(seg_d_init), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream_handle(a.device))
+    _check(st, "esa_scan_segment_bwd")
+    return seg_d_init
+
+
+def segment_compose(seg_gate_prod, seg_agg, boundary=None, reverse=False):
+    """Compose segment aggregates (esa_segment_compose).  seg_gate_prod, seg_agg: fp32
+    [nseg, B, H, Dh]; boundary: fp32 [B, H, Dh] or None.  Returns (carry [nseg, B, H, Dh],
+    total [B, H, Dh])."""
+    lib = load_library()
+    for name, t in (("seg_gate_prod", seg_gate_prod), ("seg_agg", seg_agg)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be an fp32 CUDA (HIP) tensor")
+    if seg_agg.shape != seg_gate_prod.shape or seg_agg.device != seg_gate_prod.device:
+        raise ValueError("seg_gate_prod and seg_agg must share shape and device")
+    p = seg_gate_prod.contiguous()
+    x = seg_agg.contiguous()
+    nseg = p.shape[0]
+    lanes = p[0].numel()
+    if boundary is not None:
+        _out("boundary", boundary, p.shape[1:], torch.float32, p.device)
+    carry = torch.empty_like(p)
+    total = torch.empty(p.shape[1:], dtype=torch.float32, device=p.device)
+    with _OnDevice(p.device.index):
+        st = lib.esa_segment_compose(nseg, lanes, 1 if reverse else 0, _ptr(p), _ptr(x),
+                                     _ptr(boundary), _ptr(carry), _ptr(total),
+                                     _stream_handle(p.device))
+    _check(st, "esa_segment_compose")
+    return carry, total

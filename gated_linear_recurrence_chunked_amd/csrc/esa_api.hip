@@ -193,6 +193,93 @@ std::atomic<uint32_t> g_epoch{(uint32_t)(std::chrono::steady_clock::now().time_s
 
 uint32_t next_epoch() { return g_epoch.fetch_add(1, std::memory_order_relaxed) & 0x3fffffffu; }
 
+// The backward with optional gradient outputs: da, dv, dq all given (esa_scan_bwd) or all
+// NULL (esa_scan_segment_bwd, which writes only the gradient reaching the initial state).
+int scan_bwd_impl(bool grads, int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
+                  const void* gate_logit, const void* value, const void* query,
+                  const float* init_state, const void* dy, const float* d_final_state,
+                  const float* ckpt, void* d_gate_logit, void* d_value, void* d_query,
+                  float* d_init_state, void* workspace, size_t workspace_bytes, void* stream) {
+    Problem pr;
+    int rc = check_sizes(B, T, H, Dh, dtype, mode, &pr);
+    if (rc != ESA_OK) return rc;
+    if (T > 0 && (!gate_logit || !value || !query || !dy)) return ESA_ERR_INVALID_ARG;
+    if (grads ? (T > 0 && (!d_gate_logit || !d_value || !d_query))
+              : (d_gate_logit || d_value || d_query || !d_init_state))
+        return ESA_ERR_INVALID_ARG;
+    const void* ptrs[] = {gate_logit, value, query, init_state, dy, d_final_state, ckpt,
+                          d_gate_logit, d_value, d_query, d_init_state, workspace};
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return ESA_ERR_INVALID_ARG;
+    Layout L;
+    rc = layout_of(pr, &L);
+    if (rc != ESA_OK) return rc;
+    const size_t seq = (size_t)(pr.nElem * pr.esize), st = (size_t)(pr.nLanes * 4);
+    const size_t ckb = esa_scan_ckpt_bytes(B, T, H, Dh);
+    const Range in[] = {{gate_logit, seq}, {value, seq}, {query, seq}, {init_state, st},
+                        {dy, seq}, {d_final_state, st}, {ckpt, ckb}};
+    const Range out[] = {{d_gate_logit, seq}, {d_value, seq}, {d_query, seq}, {d_init_state, st},
+                         {workspace, workspace_bytes}};
+    if (any_overlap(in, 7, out, 5)) return ESA_ERR_INVALID_ARG;
+    if (T > 0 && (!workspace || workspace_bytes < L.total)) return ESA_ERR_WORKSPACE;
+
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (d_init_state) return hip_status(launch_copy_f32(d_init_state, d_final_state, pr.nLanes, s));
+        return ESA_OK;
+    }
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* hdr = reinterpret_cast<uint32_t*>(ws);
+    uint64_t* fx = reinterpret_cast<uint64_t*>(ws + L.offX);
+    uint64_t* fy = reinterpret_cast<uint64_t*>(ws + L.offY);
+    const float* ck = ckpt;
+    if (!ck) {
+        // no checkpoint from the caller: one state-only forward pass into the workspace
+        FwdParams f;
+        memset(&f, 0, sizeof(f));
+        f.a = gate_logit;
+        f.v = value;
+        f.e0 = init_state;
+        f.ckpt = reinterpret_cast<float*>(ws + L.offCk);
+        f.hdr = hdr;
+        f.flagX = fx;
+        f.flagY = fy;
+        f.T = pr.T;
+        f.C = pr.C;
+        f.nLanes = pr.nLanes;
+        f.nck = L.nck;
+        f.nCB = L.nCB;
+        f.nTiles = L.nTilesF;
+        f.epoch = next_epoch();
+        rc = hip_status(ESA_DISPATCH(fwd, dtype, mode, Dh, f, s));
+        if (rc != ESA_OK) return rc;
+        ck = f.ckpt;
+    }
+    BwdParams p;
+    p.a = gate_logit;
+    p.v = value;
+    p.q = query;
+    p.dy = dy;
+    p.e0 = init_state;
+    p.dET = d_final_state;
+    p.ckpt = ck;
+    p.da = d_gate_logit;
+    p.dv = d_value;
+    p.dq = d_query;
+    p.de0 = d_init_state;
+    p.hdr = hdr;
+    p.flagX = fx;
+    p.flagY = fy;
+    p.T = pr.T;
+    p.C = pr.C;
+    p.nLanes = pr.nLanes;
+    p.nck = L.nck;
+    p.nCB = L.nCB;
+    p.nTiles = L.nTilesB;
+    p.epoch = next_epoch();
+    return hip_status(ESA_DISPATCH(bwd, dtype, mode, Dh, p, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -269,6 +356,7 @@ int esa_scan_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mod
     p.y = y;
     p.eT = final_state;
     p.ckpt = ckpt;
+    p.prod = nullptr;
     p.hdr = reinterpret_cast<uint32_t*>(ws);
     p.flagX = reinterpret_cast<uint64_t*>(ws + L.offX);
     p.flagY = reinterpret_cast<uint64_t*>(ws + L.offY);
@@ -287,82 +375,9 @@ int esa_scan_bwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mod
                  const float* init_state, const void* dy, const float* d_final_state,
                  const float* ckpt, void* d_gate_logit, void* d_value, void* d_query,
                  float* d_init_state, void* workspace, size_t workspace_bytes, void* stream) {
-    Problem pr;
-    int rc = check_sizes(B, T, H, Dh, dtype, mode, &pr);
-    if (rc != ESA_OK) return rc;
-    if (T > 0 && (!gate_logit || !value || !query || !dy || !d_gate_logit || !d_value || !d_query))
-        return ESA_ERR_INVALID_ARG;
-    const void* ptrs[] = {gate_logit, value, query, init_state, dy, d_final_state, ckpt,
-                          d_gate_logit, d_value, d_query, d_init_state, workspace};
-    for (const void* q : ptrs)
-        if (q && !aligned16(q)) return ESA_ERR_INVALID_ARG;
-    Layout L;
-    rc = layout_of(pr, &L);
-    if (rc != ESA_OK) return rc;
-    const size_t seq = (size_t)(pr.nElem * pr.esize), st = (size_t)(pr.nLanes * 4);
-    const size_t ckb = esa_scan_ckpt_bytes(B, T, H, Dh);
-    const Range in[] = {{gate_logit, seq}, {value, seq}, {query, seq}, {init_state, st},
-                        {dy, seq}, {d_final_state, st}, {ckpt, ckb}};
-    const Range out[] = {{d_gate_logit, seq}, {d_value, seq}, {d_query, seq}, {d_init_state, st},
-                         {workspace, workspace_bytes}};
-    if (any_overlap(in, 7, out, 5)) return ESA_ERR_INVALID_ARG;
-    if (T > 0 && (!workspace || workspace_bytes < L.total)) return ESA_ERR_WORKSPACE;
-
-    hipStream_t s = (hipStream_t)stream;
-    if (T == 0) {
-        if (d_init_state) return hip_status(launch_copy_f32(d_init_state, d_final_state, pr.nLanes, s));
-        return ESA_OK;
-    }
-    char* ws = static_cast<char*>(workspace);
-    uint32_t* hdr = reinterpret_cast<uint32_t*>(ws);
-    uint64_t* fx = reinterpret_cast<uint64_t*>(ws + L.offX);
-    uint64_t* fy = reinterpret_cast<uint64_t*>(ws + L.offY);
-    const float* ck = ckpt;
-    if (!ck) {
-        // no checkpoint from the caller: one state-only forward pass into the workspace
-        FwdParams f;
-        memset(&f, 0, sizeof(f));
-        f.a = gate_logit;
-        f.v = value;
-        f.e0 = init_state;
-        f.ckpt = reinterpret_cast<float*>(ws + L.offCk);
-        f.hdr = hdr;
-        f.flagX = fx;
-        f.flagY = fy;
-        f.T = pr.T;
-        f.C = pr.C;
-        f.nLanes = pr.nLanes;
-        f.nck = L.nck;
-        f.nCB = L.nCB;
-        f.nTiles = L.nTilesF;
-        f.epoch = next_epoch();
-        rc = hip_status(ESA_DISPATCH(fwd, dtype, mode, Dh, f, s));
-        if (rc != ESA_OK) return rc;
-        ck = f.ckpt;
-    }
-    BwdParams p;
-    p.a = gate_logit;
-    p.v = value;
-    p.q = query;
-    p.dy = dy;
-    p.e0 = init_state;
-    p.dET = d_final_state;
-    p.ckpt = ck;
-    p.da = d_gate_logit;
-    p.dv = d_value;
-    p.dq = d_query;
-    p.de0 = d_init_state;
-    p.hdr = hdr;
-    p.flagX = fx;
-    p.flagY = fy;
-    p.T = pr.T;
-    p.C = pr.C;
-    p.nLanes = pr.nLanes;
-    p.nck = L.nck;
-    p.nCB = L.nCB;
-    p.nTiles = L.nTilesB;
-    p.epoch = next_epoch();
-    return hip_status(ESA_DISPATCH(bwd, dtype, mode, Dh, p, s));
+    return scan_bwd_impl(true, B, T, H, Dh, dtype, mode, gate_logit, value, query, init_state, dy,
+                         d_final_state, ckpt, d_gate_logit, d_value, d_query, d_init_state,
+                         workspace, workspace_bytes, stream);
 }
 
 int esa_state_step(int64_t B, int64_t H, int64_t Dh, int dtype, int mode, const void* gate_logit,
@@ -386,6 +401,81 @@ int esa_state_step(int64_t B, int64_t H, int64_t Dh, int dtype, int mode, const 
     p.y = y;
     p.nLanes = pr.nLanes;
     return hip_status(ESA_DISPATCH(step, dtype, mode, Dh, p, (hipStream_t)stream));
+}
+
+int esa_scan_segment_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
+                         const void* gate_logit, const void* value, float* seg_state,
+                         float* seg_gate_prod, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    Problem pr;
+    int rc = check_sizes(B, T, H, Dh, dtype, mode, &pr);
+    if (rc != ESA_OK) return rc;
+    if (!seg_state || !seg_gate_prod) return ESA_ERR_INVALID_ARG;
+    if (T > 0 && (!gate_logit || !value)) return ESA_ERR_INVALID_ARG;
+    const void* ptrs[] = {gate_logit, value, seg_state, seg_gate_prod, workspace};
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return ESA_ERR_INVALID_ARG;
+    Layout L;
+    rc = layout_of(pr, &L);
+    if (rc != ESA_OK) return rc;
+    const size_t seq = (size_t)(pr.nElem * pr.esize), st = (size_t)(pr.nLanes * 4);
+    const Range in[] = {{gate_logit, seq}, {value, seq}};
+    const Range out[] = {{seg_state, st}, {seg_gate_prod, st}, {workspace, workspace_bytes}};
+    if (any_overlap(in, 2, out, 3)) return ESA_ERR_INVALID_ARG;
+    if (T > 0 && (!workspace || workspace_bytes < L.total)) return ESA_ERR_WORKSPACE;
+
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {  // the identity pair: zero state, unit product
+        rc = hip_status(launch_fill_f32(seg_state, 0.0f, pr.nLanes, s));
+        if (rc != ESA_OK) return rc;
+        return hip_status(launch_fill_f32(seg_gate_prod, 1.0f, pr.nLanes, s));
+    }
+    char* ws = static_cast<char*>(workspace);
+    FwdParams f;
+    memset(&f, 0, sizeof(f));
+    f.a = gate_logit;
+    f.v = value;
+    f.eT = seg_state;
+    f.prod = seg_gate_prod;
+    f.hdr = reinterpret_cast<uint32_t*>(ws);
+    f.flagX = reinterpret_cast<uint64_t*>(ws + L.offX);
+    f.flagY = reinterpret_cast<uint64_t*>(ws + L.offY);
+    f.T = pr.T;
+    f.C = pr.C;
+    f.nLanes = pr.nLanes;
+    f.nck = L.nck;
+    f.nCB = L.nCB;
+    f.nTiles = L.nTilesF;
+    f.epoch = next_epoch();
+    return hip_status(ESA_DISPATCH(fwd, dtype, mode, Dh, f, s));
+}
+
+int esa_scan_segment_bwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
+                         const void* gate_logit, const void* value, const void* query,
+                         const float* init_state, const void* dy, const float* ckpt,
+                         float* seg_d_init, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    return scan_bwd_impl(false, B, T, H, Dh, dtype, mode, gate_logit, value, query, init_state, dy,
+                         nullptr, ckpt, nullptr, nullptr, nullptr, seg_d_init, workspace,
+                         workspace_bytes, stream);
+}
+
+int esa_segment_compose(int64_t nseg, int64_t nLanes, int reverse, const float* seg_gate_prod,
+                        const float* seg_agg, const float* boundary, float* carry, float* total,
+                        void* stream) {
+    if (nseg < 1 || nLanes < 1 || (reverse != 0 && reverse != 1)) return ESA_ERR_INVALID_ARG;
+    if (!seg_gate_prod || !seg_agg || !carry) return ESA_ERR_INVALID_ARG;
+    int64_t n, bytes;
+    if (!mul64(nseg, nLanes, &n) || !mul64(n, 4, &bytes)) return ESA_ERR_INVALID_ARG;
+    const void* ptrs[] = {seg_gate_prod, seg_agg, boundary, carry, total};
+    for (const void* q : ptrs)
+        if (q && (reinterpret_cast<uintptr_t>(q) & 3u)) return ESA_ERR_INVALID_ARG;
+    const Range in[] = {{seg_gate_prod, (size_t)bytes}, {seg_agg, (size_t)bytes},
+                        {boundary, (size_t)nLanes * 4}};
+    const Range out[] = {{carry, (size_t)bytes}, {total, (size_t)nLanes * 4}};
+    if (any_overlap(in, 3, out, 2)) return ESA_ERR_INVALID_ARG;
+    return hip_status(launch_compose(nseg, nLanes, reverse, seg_gate_prod, seg_agg, boundary,
+                                     carry, total, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -23,7 +23,7 @@
 
 namespace esa {
 
-template <typename T, int MODE, int DH, int L, int NT, bool FULL>
+template <typename T, int MODE, int DH, int L, int NT, bool GRADS, bool FULL>
 __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint32_t cb, float* sP,
                                          float* sE, float* sWP, float* sWE, float* sCarry) {
     using G = Geom<T, DH, L, NT>;
@@ -176,10 +176,12 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
             const float su = MODE == kDirect ? U_[i][e] : S_[i][e] * U_[i][e];
             V_[i][e] = MODE == kDirect ? Eprev[e] * su : (Eprev[e] - V_[i][e]) * su;
         }
-        if constexpr (FULL)
-            stbuf(static_cast<char*>(p.dq) + row0 + i * rstride, voff, pack<T>(dqv));
-        else if (ok)
-            st16(p.dq, base + i * p.C, ES, pack<T>(dqv));
+        if constexpr (GRADS) {
+            if constexpr (FULL)
+                stbuf(static_cast<char*>(p.dq) + row0 + i * rstride, voff, pack<T>(dqv));
+            else if (ok)
+                st16(p.dq, base + i * p.C, ES, pack<T>(dqv));
+        }
     }
 
     // ---- reverse fold of the thread's steps: lam_out = P * lam_in + E ----
@@ -241,17 +243,19 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
             dav[e] = dE * V_[i][e];
             dvv[e] = MODE == kDirect ? dE : dE * U_[i][e];
         }
-        if constexpr (FULL) {
-            stbuf(static_cast<char*>(p.da) + row0 + i * rstride, voff, pack<T>(dav));
-            stbuf(static_cast<char*>(p.dv) + row0 + i * rstride, voff, pack<T>(dvv));
-        } else if (ok) {
-            st16(p.da, base + i * p.C, ES, pack<T>(dav));
-            st16(p.dv, base + i * p.C, ES, pack<T>(dvv));
+        if constexpr (GRADS) {
+            if constexpr (FULL) {
+                stbuf(static_cast<char*>(p.da) + row0 + i * rstride, voff, pack<T>(dav));
+                stbuf(static_cast<char*>(p.dv) + row0 + i * rstride, voff, pack<T>(dvv));
+            } else if (ok) {
+                st16(p.da, base + i * p.C, ES, pack<T>(dav));
+                st16(p.dv, base + i * p.C, ES, pack<T>(dvv));
+            }
         }
     }
 }
 
-template <typename T, int MODE, int DH, int L, int NT>
+template <typename T, int MODE, int DH, int L, int NT, bool GRADS>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     using G = Geom<T, DH, L, NT>;
     constexpr int CB = G::CB, TT = G::TT, NW = G::NW;
@@ -269,15 +273,19 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     const bool full = (int64_t)(tile + 1) * TT <= p.T && (int64_t)(cb + 1) * CB <= p.nLanes &&
                       p.C % CB == 0 && (int64_t)TT * p.C * (int64_t)sizeof(T) < (int64_t(1) << 31);
     if (full)
-        bwd_tile<T, MODE, DH, L, NT, true>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
+        bwd_tile<T, MODE, DH, L, NT, GRADS, true>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
     else
-        bwd_tile<T, MODE, DH, L, NT, false>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
+        bwd_tile<T, MODE, DH, L, NT, GRADS, false>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
 }
 
 template <typename T, int MODE, int DH>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
     using C = BwdCfg<T, DH>;
-    hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT>), dim3(p.nCB * p.nTiles), dim3(C::NT), 0, s, p);
+    const dim3 grid(p.nCB * p.nTiles), block(C::NT);
+    if (p.da)
+        hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT, true>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT, false>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 

@@ -149,6 +149,7 @@ struct FwdParams {
     void* y;          // NULL: no readout
     float* eT;
     float* ckpt;
+    float* prod;      // non-NULL (state-only pass): product of every gate over T, per lane
     uint32_t* hdr;
     uint64_t* flagX;
     uint64_t* flagY;
@@ -169,7 +170,7 @@ struct BwdParams {
     const float* e0;
     const float* dET;
     const float* ckpt;
-    void* da;
+    void* da;   // da, dv, dq all NULL: only de0 is written (sequence-segment aggregate)
     void* dv;
     void* dq;
     float* de0;
@@ -203,6 +204,10 @@ template <typename T, int MODE, int DH>
 hipError_t launch_step(const StepParams& p, hipStream_t s);
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);
+hipError_t launch_fill_f32(float* dst, float value, int64_t n, hipStream_t s);
+hipError_t launch_compose(int64_t nseg, int64_t nLanes, int reverse, const float* prod,
+                          const float* agg, const float* boundary, float* carry, float* total,
+                          hipStream_t s);
 
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
 
@@ -534,18 +539,33 @@ __device__ __forceinline__ float word_val(uint64_t w) {
 // sticky abort word of the workspace header and returns NaN, and every other waiting
 // workgroup that sees the abort word returns NaN too, so a broken chain drains instead of
 // hanging.  A correct run never comes near the limit (about a second of polling).
+//
+// With PROD (sequence-segment aggregates) a tile's inclusive word in flagY holds the product
+// of every gate from the chain's start through that tile; *pinc then receives the product
+// through the tile before `tile` (NaN when the wait gave up).
 constexpr uint32_t kSpinLimit = 1u << 20;
 
+template <bool PROD = false>
 __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t* flagY,
                                            int64_t nLanes, int64_t lane, int64_t tile, int step,
-                                           uint32_t tagAgg, uint32_t tagInc, uint32_t* hdr) {
+                                           uint32_t tagAgg, uint32_t tagInc, uint32_t* hdr,
+                                           float* pinc = nullptr) {
     float ap = 1.0f, ae = 0.0f;
     int64_t j = tile + step;
     uint32_t polls = 0;
     for (;;) {
         const uint64_t x = peek(flagX + j * nLanes + lane);
         const uint32_t tg = word_tag(x);
-        if (tg == tagInc) return ae + ap * word_val(x);
+        if (tg == tagInc) {
+            if constexpr (!PROD) return ae + ap * word_val(x);
+            // the inclusive product is published beside the inclusive state, in no fixed
+            // order: wait until it is visible too
+            const uint64_t yv = peek(flagY + j * nLanes + lane);
+            if (word_tag(yv) == tagInc) {
+                *pinc = ap * word_val(yv);
+                return ae + ap * word_val(x);
+            }
+        }
         if (tg == tagAgg) {
             const uint64_t yv = peek(flagY + j * nLanes + lane);
             if (word_tag(yv) == tagAgg) {
@@ -557,10 +577,11 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
         }
         ++polls;
         if ((polls & 255u) == 0u) {
-            if (__hip_atomic_load(&hdr[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
-                return __builtin_nanf("");
-            if (polls >= kSpinLimit) {
-                __hip_atomic_store(&hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool abort =
+                __hip_atomic_load(&hdr[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+            if (abort || polls >= kSpinLimit) {
+                if (!abort) __hip_atomic_store(&hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if constexpr (PROD) *pinc = __builtin_nanf("");
                 return __builtin_nanf("");
             }
         }

@@ -16,7 +16,7 @@
 
 namespace esa {
 
-template <typename T, int MODE, int DH, int L, int NT, bool READOUT, bool FULL>
+template <typename T, int MODE, int DH, int L, int NT, bool READOUT, bool PROD, bool FULL>
 __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint32_t cb,
                                          float* sP, float* sE, float* sWP, float* sWE,
                                          float* sCarry) {
@@ -113,13 +113,19 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         float carry = 0.0f;
         if (FULL || gl < p.nLanes) {
             uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
+            uint64_t* Y = p.flagY + (int64_t)tile * p.nLanes + gl;
+            float pin = 1.0f;  // PROD: product of the gates of every earlier tile
             if (tile == 0) {
                 carry = p.e0 ? p.e0[gl] : 0.0f;
             } else {
                 publish(X, tagAgg, te);
-                publish(p.flagY + (int64_t)tile * p.nLanes + gl, tagAgg, tp);
-                carry = look_back(p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg, tagInc,
-                                  p.hdr);
+                publish(Y, tagAgg, tp);
+                carry = look_back<PROD>(p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg, tagInc,
+                                        p.hdr, &pin);
+            }
+            if constexpr (PROD) {
+                publish(Y, tagInc, tp * pin);
+                if (tile == p.nTiles - 1) p.prod[gl] = tp * pin;
             }
             publish(X, tagInc, te + tp * carry);
         }
@@ -172,8 +178,9 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
     }
 }
 
-template <typename T, int MODE, int DH, int L, int NT, bool READOUT>
+template <typename T, int MODE, int DH, int L, int NT, bool READOUT, bool PROD>
 __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
+    static_assert(!(READOUT && PROD), "the gate product comes from the state-only pass");
     using G = Geom<T, DH, L, NT>;
     constexpr int CB = G::CB, TT = G::TT, NW = G::NW, S = G::S;
     __shared__ __attribute__((aligned(16))) float sP[S * CB];  // per-slot pairs
@@ -189,9 +196,9 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     const bool full = (int64_t)(tile + 1) * TT <= p.T && (int64_t)(cb + 1) * CB <= p.nLanes &&
                       p.C % CB == 0 && (int64_t)TT * p.C * (int64_t)sizeof(T) < (int64_t(1) << 31);
     if (full)
-        fwd_tile<T, MODE, DH, L, NT, READOUT, true>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
+        fwd_tile<T, MODE, DH, L, NT, READOUT, PROD, true>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
     else
-        fwd_tile<T, MODE, DH, L, NT, READOUT, false>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
+        fwd_tile<T, MODE, DH, L, NT, READOUT, PROD, false>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
 }
 
 template <typename T, int MODE, int DH>
@@ -199,9 +206,11 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
     using C = FwdCfg<T, DH>;
     const dim3 grid(p.nCB * p.nTiles), block(C::NT);
     if (p.y)
-        hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, true>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, true, false>), grid, block, 0, s, p);
+    else if (p.prod)
+        hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, false, true>), grid, block, 0, s, p);
     else
-        hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, false>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, false, false>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 

@@ -4,9 +4,10 @@
 // state) and "[ QUICK START ]" (decode_step); page "Entangled State Attention v2.1",
 // section 5 (lightning_step).  The fp32 state is updated in place.
 //
-// Also the two small utility kernels of the library: a zero fill (used instead of
-// hipMemsetAsync so that callers may capture the library's work in a graph) and an fp32
-// copy (final state of an empty sequence).
+// Also the small utility kernels of the library: a zero fill (used instead of
+// hipMemsetAsync so that callers may capture the library's work in a graph), an fp32 fill
+// and copy (states of an empty sequence), and the composition of sequence-segment
+// aggregates.
 #include "esa_common.hpp"
 
 namespace esa {
@@ -111,6 +112,51 @@ __global__ __launch_bounds__(256) void copy_f32_kernel(float* dst, const float* 
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
         dst[i] = src ? src[i] : 0.0f;
+}
+
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* dst, float value, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        dst[i] = value;
+}
+
+hipError_t launch_fill_f32(float* dst, float value, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_f32_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, dst, value, n);
+    return hipGetLastError();
+}
+
+// Composition of sequence-segment aggregates, per lane, in segment order (forward) or from
+// the last segment (reverse): the pair combine (P, E) o c = P c + E of the scan, applied to
+// the boundary value segment after segment.  carry[k] receives the value entering segment k
+// from its earlier side (forward: the state at its start; reverse: the gradient at its end);
+// total receives the value after the last one.
+__global__ __launch_bounds__(256) void compose_kernel(int64_t nseg, int64_t nLanes, int reverse,
+                                                      const float* prod, const float* agg,
+                                                      const float* boundary, float* carry,
+                                                      float* total) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t l = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; l < nLanes; l += stride) {
+        float c = boundary ? boundary[l] : 0.0f;
+        for (int64_t q = 0; q < nseg; ++q) {
+            const int64_t k = reverse ? nseg - 1 - q : q;
+            carry[k * nLanes + l] = c;
+            c = prod[k * nLanes + l] * c + agg[k * nLanes + l];
+        }
+        if (total) total[l] = c;
+    }
+}
+
+hipError_t launch_compose(int64_t nseg, int64_t nLanes, int reverse, const float* prod,
+                          const float* agg, const float* boundary, float* carry, float* total,
+                          hipStream_t s) {
+    int64_t blocks = (nLanes + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(compose_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, nseg, nLanes,
+                       reverse, prod, agg, boundary, carry, total);
+    return hipGetLastError();
 }
 
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s) {

@@ -50,7 +50,8 @@
 extern "C" {
 #endif
 
-/* 1: fp32 / fp16 / bf16 storage.  2: adds the fp8 storage dtypes ESA_F8E4M3, ESA_F8E5M2. */
+/* 1: fp32 / fp16 / bf16 storage.  2: adds the fp8 storage dtypes ESA_F8E4M3, ESA_F8E5M2
+ * and the sequence-segment calls. */
 #define ESA_ABI_VERSION 2
 
 /* Checkpoint granularity: the forward can store the fp32 state at every 64th step. */
@@ -151,6 +152,59 @@ int esa_scan_bwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mod
 int esa_state_step(int64_t B, int64_t H, int64_t Dh, int dtype, int mode,
                    const void *gate_logit, const void *value, const void *query, float *state,
                    void *y, void *stream);
+
+/* ---- Sequence segments: the scan over T split into consecutive segments ----
+ *
+ * The recurrence composes associatively (page "Entangled State Attention", "[ ARCHITECTURE ]"),
+ * so a sequence cut into segments 0..n-1 (one per device, say) is scanned in two passes:
+ *   1. each segment's aggregate over its own steps from a zero state: the state it produces,
+ *      E_seg, and the product of its gates, P_seg (esa_scan_segment_fwd, reads a and v only);
+ *   2. the aggregates of all segments composed in order (esa_segment_compose), giving the
+ *      state entering each segment; each segment then runs esa_scan_fwd with that state as
+ *      init_state.
+ * The backward mirrors it: each segment's gradient reaching its start with no gradient
+ * arriving at its end (esa_scan_segment_bwd), the composition from the last segment
+ * (esa_segment_compose, reverse = 1, with the same P_seg), then esa_scan_bwd per segment
+ * with that gradient as d_final_state.  Results equal the unsegmented scan up to fp32
+ * rounding order. */
+
+/* Segment aggregate (pass 1).  Over this call's T steps from a zero state:
+ *   seg_state      [B,H,Dh] fp32, out: E_{T-1}
+ *   seg_gate_prod  [B,H,Dh] fp32, out: the product over t of A_t = sigma(a_t)
+ * T = 0 gives the identity (zeros and ones).  Sizes, dtypes, modes, alignment, workspace and
+ * errors as esa_scan_fwd. */
+int esa_scan_segment_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
+                         const void *gate_logit, const void *value, float *seg_state,
+                         float *seg_gate_prod, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* Backward segment aggregate: the gradient reaching the segment's initial state when no
+ * gradient arrives at its final state (d_final_state = 0), i.e. esa_scan_bwd's d_init_state
+ * without writing the sequence gradients.
+ *   gate_logit, value, query, init_state, dy, ckpt   as esa_scan_bwd (init_state is the
+ *                  state entering the segment; ckpt from its esa_scan_fwd, or NULL)
+ *   seg_d_init     [B,H,Dh] fp32, out */
+int esa_scan_segment_bwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
+                         const void *gate_logit, const void *value, const void *query,
+                         const float *init_state, const void *dy, const float *ckpt,
+                         float *seg_d_init, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* Composition of segment aggregates (pass 2), per lane, c <- P_k c + X_k segment by segment:
+ *   nseg, nLanes   segments and lanes (nLanes = B*H*Dh)
+ *   reverse        0: segments 0..n-1 in order; 1: from segment n-1 down to 0
+ *   seg_gate_prod  [nseg, nLanes] fp32, in: P_k of each segment
+ *   seg_agg        [nseg, nLanes] fp32, in: X_k = seg_state (forward) or seg_d_init (reverse)
+ *   boundary       [nLanes] fp32, in: init_state (forward) or d_final_state (reverse) of the
+ *                  whole sequence, or NULL for zeros
+ *   carry          [nseg, nLanes] fp32, out: the value entering segment k from its earlier
+ *                  side: its init_state (forward) or its d_final_state (reverse)
+ *   total          [nLanes] fp32, out, or NULL: the value after the last segment: the final
+ *                  state (forward) or d_init_state of the whole sequence (reverse)
+ * Pointers need 4-byte alignment; outputs may not overlap inputs or each other. */
+int esa_segment_compose(int64_t nseg, int64_t nLanes, int reverse, const float *seg_gate_prod,
+                        const float *seg_agg, const float *boundary, float *carry, float *total,
+                        void *stream);
 
 #ifdef __cplusplus
 }

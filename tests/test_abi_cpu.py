@@ -151,3 +151,44 @@ def test_step_validation(lib):
 def test_workspace_init_validation(lib):
     assert lib.esa_workspace_init(None, 256, None) == INVALID
     assert lib.esa_workspace_init(ctypes.c_void_p(0x100000008), 256, None) == INVALID
+
+
+def test_segment_validation(lib):
+    def seg_fwd(B=2, T=100, H=2, Dh=64, dt=1, mode=1, a=1, v=2, st=3, pr=4, ws=5, wsb=0):
+        p = [None if x is None else (x if isinstance(x, ctypes.c_void_p) else addr(x))
+             for x in (a, v, st, pr, ws)]
+        return lib.esa_scan_segment_fwd(B, T, H, Dh, dt, mode, *p[:4], p[4], wsb, None)
+
+    assert seg_fwd(st=None) == INVALID
+    assert seg_fwd(pr=None) == INVALID
+    assert seg_fwd(a=None) == INVALID
+    assert seg_fwd(dt=5) == INVALID
+    assert seg_fwd(Dh=48) == UNSUPPORTED
+    assert seg_fwd(v=ctypes.c_void_p(0x100000000 + 8)) == INVALID
+    assert seg_fwd(st=4) == INVALID  # the two outputs overlap
+    assert seg_fwd(ws=None) == WORKSPACE
+
+    def seg_bwd(B=2, T=100, H=2, Dh=64, dt=2, mode=0, a=1, v=2, q=3, e0=None, dy=4, ck=None,
+                out=5, ws=6):
+        p = [None if x is None else addr(x) for x in (a, v, q, e0, dy, ck, out, ws)]
+        return lib.esa_scan_segment_bwd(B, T, H, Dh, dt, mode, *p[:7], p[7], 0, None)
+
+    assert seg_bwd(out=None) == INVALID
+    assert seg_bwd(dy=None) == INVALID
+    assert seg_bwd(out=4) == INVALID  # output overlaps dy
+    assert seg_bwd(ws=None) == WORKSPACE
+
+    def compose(nseg=3, lanes=64, rev=0, p=1, x=2, bnd=None, carry=3, total=None):
+        ptr = [None if k is None else (k if isinstance(k, ctypes.c_void_p) else addr(k))
+               for k in (p, x, bnd, carry, total)]
+        return lib.esa_segment_compose(nseg, lanes, rev, *ptr, None)
+
+    assert compose(nseg=0) == INVALID
+    assert compose(lanes=0) == INVALID
+    assert compose(rev=2) == INVALID
+    assert compose(p=None) == INVALID
+    assert compose(carry=None) == INVALID
+    assert compose(carry=1) == INVALID  # carry overlaps the products
+    assert compose(total=3) == INVALID  # total overlaps carry
+    assert compose(x=ctypes.c_void_p(0x100000000 + 0x20000000 + 2)) == INVALID  # misaligned
+    assert compose(nseg=1 << 40, lanes=1 << 40) == INVALID  # size overflows
