@@ -230,6 +230,91 @@ def bench_decode(args, torch, binding, synth):
     return res
 
 
+def bench_variants(args, torch, binding, synth):
+    """Two variants beside the headline, each timed with HIP events over 5 repetitions:
+    fp8 (E4M3) storage on the 64K workload's shapes and draws, and one device's share of the
+    64K workload cut into 8 sequence segments (T = 8192 per device), run through the
+    two-pass segmented protocol against a plain scan of the same shape."""
+    out = {}
+    reps = 5
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    wl = synth.WORKLOADS["long64k_f8e4m3"]
+    B, T, H, Dh = wl.B, wl.T, wl.H, wl.Dh
+    log(f"[bench] variant {wl.name}")
+    g = synth.make_inputs(wl, device="cuda:0", with_dy=True)
+    nelem = B * T * H * Dh
+    ckb = binding.ckpt_bytes(B, T, H, Dh)
+    y = torch.empty_like(g["a"])
+    eT = torch.empty((B, H, Dh), dtype=torch.float32, device="cuda:0")
+    ck = {}
+
+    def fwd():
+        ck["c"] = binding.scan_fwd(g["a"], g["v"], g["q"], mode=wl.mode, return_ckpt=True,
+                                   final_state=eT, y=y)[2]
+
+    fwd_ms = timed(fwd)
+    bwd_ms = timed(lambda: binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], ckpt=ck["c"],
+                                            mode=wl.mode))
+    fb = nelem * 4 + ckb + B * H * Dh * 4
+    bb = nelem * 7 + ckb
+    out[wl.name] = {"B": B, "T": T, "H": H, "Dh": Dh, "storage": "f8e4m3", "mode": wl.mode,
+                    "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+                    "fwd_GB_s": round(fb / (fwd_ms * 1e-3) / 1e9, 1),
+                    "bwd_GB_s": round(bb / (bwd_ms * 1e-3) / 1e9, 1),
+                    "tokens_per_s": B * T / ((fwd_ms + bwd_ms) * 1e-3)}
+    del g, y, eT, ck
+    torch.cuda.empty_cache()
+
+    nseg = 8
+    wl = synth.WORKLOADS["long64k_f16"]
+    B, T, H, Dh = wl.B, wl.T // nseg, wl.H, wl.Dh
+    log(f"[bench] variant: one of {nseg} sequence segments of {wl.name} (T={T})")
+    g = synth.make_inputs(wl, device="cuda:0", T=T, with_dy=True)
+    st = {}
+
+    def plain():
+        _, _, c = binding.scan_fwd(g["a"], g["v"], g["q"], mode=wl.mode, return_ckpt=True)
+        binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], ckpt=c, mode=wl.mode)
+
+    def segmented():
+        # this device's aggregate; the other devices' aggregates would arrive by an
+        # all-gather, stood in for here by copies of this one (the composition's cost does
+        # not depend on the values)
+        e, pr = binding.segment_fwd(g["a"], g["v"], mode=wl.mode)
+        carry, _ = binding.segment_compose(pr.expand(nseg, -1, -1, -1),
+                                           e.expand(nseg, -1, -1, -1))
+        k = nseg // 2
+        _, _, c = binding.scan_fwd(g["a"], g["v"], g["q"], carry[k], mode=wl.mode,
+                                   return_ckpt=True)
+        lam = binding.segment_bwd(g["a"], g["v"], g["q"], g["dy"], carry[k], ckpt=c, mode=wl.mode)
+        dcarry, _ = binding.segment_compose(pr.expand(nseg, -1, -1, -1),
+                                            lam.expand(nseg, -1, -1, -1), reverse=True)
+        binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], carry[k], dcarry[k], ckpt=c,
+                         mode=wl.mode)
+
+    plain_ms = timed(plain)
+    seg_ms = timed(segmented)
+    out[f"{wl.name}_segment_of_{nseg}"] = {
+        "B": B, "T_per_device": T, "H": H, "Dh": Dh, "plain_fwd_bwd_ms": round(plain_ms, 4),
+        "segmented_fwd_bwd_ms": round(seg_ms, 4), "overhead": round(seg_ms / plain_ms, 3),
+        "note": "one device's kernels only; the all-gathers of the segment aggregates "
+                "(2 x B*H*Dh fp32 per device each way) are not run"}
+    del g
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(args, train):
     """The oracle, as it stands, on a bounded sample of the 64K workload: whole batch rows
     (every row is an independent problem), one row per thread, fwd + bwd."""
@@ -417,6 +502,8 @@ def main():
     if args.only in ("decode", "all"):
         dec = bench_decode(args, torch, binding, synth)
         result["decode"] = dec
+    if args.only == "all":
+        result["variants"] = bench_variants(args, torch, binding, synth)
     if train is not None and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, train)
     print(json.dumps(result), flush=True)
