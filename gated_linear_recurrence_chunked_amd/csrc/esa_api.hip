@@ -185,13 +185,30 @@ hipError_t step_dh(int64_t Dh, const StepParams& p, hipStream_t s) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ESA_OK : ESA_ERR_HIP; }
 
-// Epochs tag the look-back words of one scan kernel launch.  The counter is process-wide and
-// only ever increments, so a workspace never sees the same epoch twice within 2^30 launches;
-// its start is drawn from the clock and the process id.
+// Epochs tag the look-back words of one scan kernel launch.  The host counter is
+// process-wide and only ever increments, so a workspace never sees the same host epoch twice
+// within 2^29 launches; its start is drawn from the clock and the process id.
 std::atomic<uint32_t> g_epoch{(uint32_t)(std::chrono::steady_clock::now().time_since_epoch().count() ^
                                          ((uint64_t)getpid() << 16))};
 
-uint32_t next_epoch() { return g_epoch.fetch_add(1, std::memory_order_relaxed) & 0x3fffffffu; }
+uint32_t next_epoch() { return g_epoch.fetch_add(1, std::memory_order_relaxed) & kHostEpochMask; }
+
+// The epoch of a scan launch about to be enqueued on s.  Eager: the host counter.  While s is
+// being recorded into a graph: the workspace's device epoch (header word 0), advanced by a
+// one-thread kernel recorded just before the launch, so every replay tags its look-back words
+// afresh.
+int set_epoch(hipStream_t s, uint32_t* hdr, uint32_t* epoch, const uint32_t** word) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return ESA_ERR_HIP;
+    if (cs == hipStreamCaptureStatusActive) {
+        *epoch = 0;
+        *word = hdr;
+        return hip_status(launch_epoch_bump(hdr, s));
+    }
+    *epoch = next_epoch();
+    *word = nullptr;
+    return ESA_OK;
+}
 
 // The backward with optional gradient outputs: da, dv, dq all given (esa_scan_bwd) or all
 // NULL (esa_scan_segment_bwd, which writes only the gradient reaching the initial state).
@@ -250,7 +267,8 @@ int scan_bwd_impl(bool grads, int64_t B, int64_t T, int64_t H, int64_t Dh, int d
         f.nck = L.nck;
         f.nCB = L.nCB;
         f.nTiles = L.nTilesF;
-        f.epoch = next_epoch();
+        rc = set_epoch(s, hdr, &f.epoch, &f.epochWord);
+        if (rc != ESA_OK) return rc;
         rc = hip_status(ESA_DISPATCH(fwd, dtype, mode, Dh, f, s));
         if (rc != ESA_OK) return rc;
         ck = f.ckpt;
@@ -276,7 +294,8 @@ int scan_bwd_impl(bool grads, int64_t B, int64_t T, int64_t H, int64_t Dh, int d
     p.nck = L.nck;
     p.nCB = L.nCB;
     p.nTiles = L.nTilesB;
-    p.epoch = next_epoch();
+    rc = set_epoch(s, hdr, &p.epoch, &p.epochWord);
+    if (rc != ESA_OK) return rc;
     return hip_status(ESA_DISPATCH(bwd, dtype, mode, Dh, p, s));
 }
 
@@ -366,7 +385,8 @@ int esa_scan_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mod
     p.nck = L.nck;
     p.nCB = L.nCB;
     p.nTiles = L.nTilesF;
-    p.epoch = next_epoch();
+    rc = set_epoch(s, p.hdr, &p.epoch, &p.epochWord);
+    if (rc != ESA_OK) return rc;
     return hip_status(ESA_DISPATCH(fwd, dtype, mode, Dh, p, s));
 }
 
@@ -446,7 +466,8 @@ int esa_scan_segment_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype,
     f.nck = L.nck;
     f.nCB = L.nCB;
     f.nTiles = L.nTilesF;
-    f.epoch = next_epoch();
+    rc = set_epoch(s, f.hdr, &f.epoch, &f.epochWord);
+    if (rc != ESA_OK) return rc;
     return hip_status(ESA_DISPATCH(fwd, dtype, mode, Dh, f, s));
 }
 

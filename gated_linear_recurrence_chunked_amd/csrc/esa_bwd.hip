@@ -30,8 +30,9 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, HL = G::HL;
     constexpr int TT = G::TT;
     constexpr int ES = sizeof(T);
-    const uint32_t tagAgg = make_tag(p.epoch, kTagAgg);
-    const uint32_t tagInc = make_tag(p.epoch, kTagInc);
+    const uint32_t epoch = launch_epoch(p.epoch, p.epochWord);
+    const uint32_t tagAgg = make_tag(epoch, kTagAgg);
+    const uint32_t tagInc = make_tag(epoch, kTagInc);
 
     const int tid = threadIdx.x;
     const int j = tid % NCL;

@@ -30,8 +30,13 @@
 //
 // Look-back words are 64-bit (tag, fp32 value) pairs written and read with single-copy
 // atomic 64-bit accesses at agent scope, so no fence is needed between a value and its
-// flag.  The tag carries a per-call epoch chosen by the host, so stale words from earlier
-// calls never match and the flag array needs no clearing between calls.
+// flag.  The tag carries a per-launch epoch, so stale words from earlier launches never
+// match and the flag array needs no clearing between calls.  An eagerly issued launch takes
+// its epoch from a host counter; a launch recorded into a graph cannot (every replay would
+// reuse the recorded value and find the previous replay's words), so it reads the epoch
+// from the workspace header, where a one-thread kernel recorded just before it advances it
+// on every replay.  The two kinds of epoch never coincide (bit 29 clear for host epochs,
+// set for device epochs).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -132,10 +137,13 @@ struct BwdCfg {
 
 // Workspace layout: [header 256 B][flag X words][flag Y words][internal checkpoint].
 struct WsHeader {
-    uint32_t reserved[3];
+    uint32_t epoch;  // device epoch of launches recorded into graphs (bit 29 set once used)
+    uint32_t reserved[2];
     uint32_t abort;  // sticky: set when a look-back wait timed out (results are then NaN)
     uint32_t pad[60];
 };
+constexpr uint32_t kHostEpochMask = 0x1fffffffu;  // host epochs: bit 29 clear
+constexpr uint32_t kDeviceEpochBit = 0x20000000u;  // device epochs: bit 29 set
 static_assert(sizeof(WsHeader) == 256, "header must be 256 bytes");
 
 constexpr uint32_t kTagAgg = 1u;
@@ -159,7 +167,8 @@ struct FwdParams {
     int64_t nck;     // ceil(T / 64)
     uint32_t nCB;
     uint32_t nTiles;
-    uint32_t epoch;  // tags of this call's look-back words
+    uint32_t epoch;  // tags of this call's look-back words (host epoch)
+    const uint32_t* epochWord;  // non-NULL: read the epoch here instead (graph-recorded launch)
 };
 
 struct BwdParams {
@@ -184,6 +193,7 @@ struct BwdParams {
     uint32_t nCB;
     uint32_t nTiles;
     uint32_t epoch;
+    const uint32_t* epochWord;
 };
 
 struct StepParams {
@@ -205,6 +215,7 @@ hipError_t launch_step(const StepParams& p, hipStream_t s);
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);
 hipError_t launch_fill_f32(float* dst, float value, int64_t n, hipStream_t s);
+hipError_t launch_epoch_bump(uint32_t* word, hipStream_t s);
 hipError_t launch_compose(int64_t nseg, int64_t nLanes, int reverse, const float* prod,
                           const float* agg, const float* boundary, float* carry, float* total,
                           hipStream_t s);
@@ -609,6 +620,12 @@ __device__ __forceinline__ void tile_of(uint32_t wg, uint32_t nCB, uint32_t& row
 
 __device__ __forceinline__ uint32_t make_tag(uint32_t epoch, uint32_t kind) {
     return (epoch << 2) | kind;
+}
+
+// The epoch of this launch: the host's, or the workspace's device epoch for a launch recorded
+// into a graph (advanced by epoch_bump_kernel before every replay of the launch).
+__device__ __forceinline__ uint32_t launch_epoch(uint32_t host_epoch, const uint32_t* word) {
+    return word ? __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : host_epoch;
 }
 
 #endif  // device compile

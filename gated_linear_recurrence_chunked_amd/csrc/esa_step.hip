@@ -128,6 +128,20 @@ hipError_t launch_fill_f32(float* dst, float value, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Advances the workspace's device epoch (bit 29 set, 29 bits of count) for the scan launch
+// recorded after it in the same graph.
+__global__ __launch_bounds__(64) void epoch_bump_kernel(uint32_t* word) {
+    if (threadIdx.x == 0) {
+        const uint32_t e = *word;
+        *word = ((e + 1u) & kHostEpochMask) | kDeviceEpochBit;
+    }
+}
+
+hipError_t launch_epoch_bump(uint32_t* word, hipStream_t s) {
+    hipLaunchKernelGGL(epoch_bump_kernel, dim3(1), dim3(64), 0, s, word);
+    return hipGetLastError();
+}
+
 // Composition of sequence-segment aggregates, per lane, in segment order (forward) or from
 // the last segment (reverse): the pair combine (P, E) o c = P c + E of the scan, applied to
 // the boundary value segment after segment.  carry[k] receives the value entering segment k

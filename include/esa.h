@@ -30,6 +30,12 @@
  * counter that tags each scan launch's look-back words.  Calls that share one workspace
  * must not run concurrently (use one workspace per stream).
  *
+ * Graphs.  Every call may be recorded into a HIP graph by stream capture.  A scan launch
+ * recorded into a graph takes its look-back tag from word 0 of the workspace, which a
+ * one-thread kernel recorded just before it advances, so each replay is correct with no host
+ * work; no call records a memset.  Replays of graphs that share a workspace must not run
+ * concurrently with each other or with eager calls on that workspace.
+ *
  * Errors.  Every entry point returns an esa_status.  All argument checks run before any
  * HIP call, so an invalid call changes nothing on the device:
  *   ESA_ERR_INVALID_ARG  null required pointer, negative size, bad enum, pointer not
