@@ -215,10 +215,9 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
             if (tile == p.nTiles - 1) {
                 carry = p.dET ? p.dET[gl] : 0.0f;
             } else {
-                publish(X, tagAgg, te);
-                publish(p.flagY + (int64_t)tile * p.nLanes + gl, tagAgg, tp);
-                carry = look_back(p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc,
-                                  p.hdr);
+                float pin;  // unused: the backward carries no gate product
+                carry = chain_carry(p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc,
+                                    p.hdr, tp, te, &pin);
             }
             const float lam_out = te + tp * carry;
             publish(X, tagInc, lam_out);

@@ -16,9 +16,10 @@
 //   level 2  slot pairs go through LDS: lane = channel of each wave scans that wave's slots,
 //            then the waves' aggregates are composed (slots_phase_a / slots_phase_b).
 //   level 3  tiles of one channel block are chained by a decoupled look-back: a tile
-//            publishes its aggregate pair, then walks back over earlier tiles' published
-//            pairs until it meets an inclusive value, then publishes its own inclusive
-//            value.
+//            whose neighbour already shows an inclusive value takes it; otherwise it
+//            publishes its aggregate pair and walks back over earlier tiles' published
+//            pairs until it meets an inclusive value.  Either way it then publishes its
+//            own inclusive value.
 //
 // Tile order.  Workgroup IDs are tile-major within each XCD (see tile_of; the backward numbers
 // tiles from the end), so a tile only ever waits on tiles with smaller IDs.  The hardware
@@ -598,6 +599,34 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
         }
         __builtin_amdgcn_s_sleep(1);
     }
+}
+
+// The carry entering `tile` on one lane's chain.  When the neighbouring tile on the earlier
+// side has already published its inclusive value -- the usual case once a chain's earlier
+// tiles were dispatched well before this one -- the tile takes it directly and publishes no
+// aggregate pair, so its only look-back traffic is its own inclusive word (8 instead of 24
+// bytes per lane; measured 0.6-2.3 % faster at 64K context).  Otherwise it publishes its
+// aggregate pair (te, tp) and walks back.  The caller then publishes the inclusive value.
+// Successors cope with a tile that never publishes an aggregate: they wait for its
+// inclusive word, which follows without any wait of its own.
+template <bool PROD = false>
+__device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, int64_t nLanes,
+                                             int64_t lane, int64_t tile, int step, uint32_t tagAgg,
+                                             uint32_t tagInc, uint32_t* hdr, float tp, float te,
+                                             float* pin) {
+    const int64_t nb = (tile + step) * nLanes + lane;
+    const uint64_t x = peek(flagX + nb);
+    if (word_tag(x) == tagInc) {
+        if constexpr (!PROD) return word_val(x);
+        const uint64_t y = peek(flagY + nb);
+        if (word_tag(y) == tagInc) {
+            *pin = word_val(y);
+            return word_val(x);
+        }
+    }
+    publish(flagX + tile * nLanes + lane, tagAgg, te);
+    publish(flagY + tile * nLanes + lane, tagAgg, tp);
+    return look_back<PROD>(flagX, flagY, nLanes, lane, tile, step, tagAgg, tagInc, hdr, pin);
 }
 
 // Workgroup -> (tile row, channel block).  Workgroup i runs on XCD i mod 8.  When the channel

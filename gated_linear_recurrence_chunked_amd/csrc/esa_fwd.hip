@@ -119,10 +119,8 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
             if (tile == 0) {
                 carry = p.e0 ? p.e0[gl] : 0.0f;
             } else {
-                publish(X, tagAgg, te);
-                publish(Y, tagAgg, tp);
-                carry = look_back<PROD>(p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg, tagInc,
-                                        p.hdr, &pin);
+                carry = chain_carry<PROD>(p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg,
+                                          tagInc, p.hdr, tp, te, &pin);
             }
             if constexpr (PROD) {
                 publish(Y, tagInc, tp * pin);
