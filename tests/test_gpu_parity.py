@@ -326,6 +326,31 @@ def test_workload_long64k_f16():
     _fwd_bwd_rows(wl, [0, 63])
 
 
+def test_long64k_shapes_in_fp32_8gib_tensors():
+    """The 64K workload's shapes and draws in fp32 storage: every sequence tensor is 8 GiB,
+    so element and byte offsets pass 2^31 and 2^32 inside a call."""
+    wl = synth.WORKLOADS["long64k_f16"]
+    say("64K shapes in fp32 (8 GiB tensors)")
+    g = synth.make_inputs(wl, device=DEV, with_dy=True, dtype="f32")
+    assert g["a"].numel() * 4 == 8 << 30
+    y, eT, ck = binding.scan_fwd(g["a"], g["v"], g["q"], mode=wl.mode, return_ckpt=True)
+    da, dv, dq, de0 = binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], ckpt=ck, mode=wl.mode)
+    torch.cuda.synchronize()
+    check_abort_clear()
+    for b in (0, 63):
+        say(f"  row {b}")
+        xa, xv, xq, xd = (rows(g[k], [b]) for k in ("a", "v", "q", "dy"))
+        ry, reT = oracle.scan_fwd(xa, xv, xq, mode=MODES[wl.mode])
+        assert_close(f"y[{b}]", rows(y, [b]), ry, torch.float32)
+        assert_close(f"eT[{b}]", rows(eT, [b]), reT, torch.float32)
+        r = oracle.scan_bwd(xa, xv, xq, xd, mode=MODES[wl.mode])
+        for name, got, ref in zip(("d_logit", "d_value", "d_query", "d_init"),
+                                  (da, dv, dq, de0), r):
+            assert_close(f"{name}[{b}]", rows(got, [b]), ref, torch.float32)
+    del g, y, eT, ck, da, dv, dq, de0
+    torch.cuda.empty_cache()
+
+
 def test_workload_long64k_f8e4m3():
     wl = synth.WORKLOADS["long64k_f8e4m3"]
     say(f"workload {wl.name}")
