@@ -124,6 +124,8 @@ def bench_train(args, torch, binding, synth):
         "B": B, "T": T, "H": H, "Dh": Dh, "nelem": nelem,
         "ms_per_step": total_ms, "wall_ms_per_step": wall * 1e3 / args.steps,
         "fwd_ms": sum(fwd_ms) / len(fwd_ms), "bwd_ms": sum(bwd_ms) / len(bwd_ms),
+        "fwd_ms_median": sorted(fwd_ms)[len(fwd_ms) // 2],
+        "bwd_ms_median": sorted(bwd_ms)[len(bwd_ms) // 2],
         "fwd_bytes": fwd_bytes, "bwd_bytes": bwd_bytes, "tokens": B * T,
     }
     out["tokens_per_s"] = B * T / (total_ms * 1e-3)
@@ -491,11 +493,13 @@ def main():
                               "avg_launch_ms": round(train[f"{dom}_ms"], 4)}
         result["stream_reference"] = train["stream_reference"]
         result["kernels"] = {
-            "fwd": {"ms": round(train["fwd_ms"], 4), "GB_s": round(train["fwd_gbs"], 1),
+            "fwd": {"ms": round(train["fwd_ms"], 4), "ms_median": round(train["fwd_ms_median"], 4),
+                    "GB_s": round(train["fwd_gbs"], 1),
                     "frac_hbm": round(train["fwd_gbs"] / HBM_PEAK_GBS, 4),
                     "tokens_per_s": train["fwd_tokens_per_s"],
                     "algorithmic_bytes": train["fwd_bytes"]},
-            "bwd": {"ms": round(train["bwd_ms"], 4), "GB_s": round(train["bwd_gbs"], 1),
+            "bwd": {"ms": round(train["bwd_ms"], 4), "ms_median": round(train["bwd_ms_median"], 4),
+                    "GB_s": round(train["bwd_gbs"], 1),
                     "frac_hbm": round(train["bwd_gbs"] / HBM_PEAK_GBS, 4),
                     "algorithmic_bytes": train["bwd_bytes"]},
         }
