@@ -31,7 +31,8 @@ class _ScanFn(torch.autograd.Function):
         y, final_state, ckpt = binding.scan_fwd(a, v, q, init_state, mode=mode, return_ckpt=True)
         ctx.mode = mode
         ctx.has_init = init_state is not None
-        ctx.save_for_backward(a, v, q, init_state if init_state is not None else ckpt, ckpt)
+        ctx.save_for_backward(a, v, q, init_state if init_state is not None else a.new_empty(0),
+                              ckpt)
         return y, final_state
 
     @staticmethod
@@ -63,6 +64,10 @@ class ESALayer(torch.nn.Module):
         self.embd, self.head, self.dh = embd, head, embd // head
         if self.dh not in (16, 32, 64, 128):
             raise ValueError("head dimension embd / head must be 16, 32, 64 or 128")
+        if dtype not in (torch.float32, torch.float16, torch.bfloat16):
+            # the projections are torch GEMMs in this dtype; 8-bit storage is reached through
+            # the scan functions of the binding directly
+            raise ValueError("ESALayer dtype must be float32, float16 or bfloat16")
         self.mode = mode
         kw = dict(device=device, dtype=dtype)
         self.W_A = torch.nn.Parameter(torch.empty(embd, embd, **kw))
