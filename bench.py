@@ -346,6 +346,115 @@ def cpu_baseline(args, train):
                       f"fwd+bwd, one row per thread, {threads} threads"}
 
 
+def bench_workloads(args, torch, binding, synth):
+    """Every synthetic workload: the GPU path's time (HIP events, inputs resident) and the
+    oracle's rate on a bounded sample of the same inputs, on 1 host thread and on N (one
+    batch row per thread).  A token is one (batch, position) over all heads and channels."""
+    import oracle
+
+    def gpu_ms(fn, target_ms=20.0):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        reps = int(max(3, min(2000, target_ms / max(e0.elapsed_time(e1), 1e-3))))
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+
+    def gpu_ms_cold(fn, reps=20):
+        """Each launch after writing 1 GiB, more than the L2 caches and the 256 MB MALL hold,
+        so the inputs come from HBM; the events bracket the scan launch only."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            flush.fill_(1)
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+
+    def oracle_rate(g, mode, rows, T_s, threads, bwd):
+        x = {k: oracle._f64(g[k][:rows, :T_s].cpu()) for k in g}
+        t0 = time.perf_counter()
+        oracle.scan_fwd(x["a"], x["v"], x["q"], mode=mode, threads=threads)
+        if bwd:
+            oracle.scan_bwd(x["a"], x["v"], x["q"], x["dy"], mode=mode, threads=threads)
+        return rows * T_s / (time.perf_counter() - t0)
+
+    if not args.no_cpu_baseline:
+        oracle._load()  # load the library outside the timed samples
+    specs = [("small_fwd_f32", None, False), ("layer_fwd_f16", None, False),
+             ("long64k_f16", None, False), ("long64k_f16", None, True),
+             ("train8k_bf16", None, True), ("long64k_f8e4m3", None, False),
+             ("long64k_f8e4m3", None, True)]
+    specs += [("decode_f16", T, False) for T in synth.WORKLOADS["decode_f16"].prompts]
+    out = []
+    for name, T_over, bwd in specs:
+        wl = synth.WORKLOADS[name]
+        T = T_over or wl.T
+        B, H, Dh = wl.B, wl.H, wl.Dh
+        log(f"[bench] workload {name} T={T} {'fwd+bwd' if bwd else 'fwd'}")
+        g = synth.make_inputs(wl, device="cuda:0", T=T, with_dy=bwd)
+        nelem = B * T * H * Dh
+        sb = g["a"].element_size()
+        y = torch.empty_like(g["a"])
+        eT = torch.empty((B, H, Dh), dtype=torch.float32, device="cuda:0")
+        if bwd:
+            ck_b = binding.ckpt_bytes(B, T, H, Dh)
+            nbytes = nelem * 4 * sb + ck_b + B * H * Dh * 4 + nelem * 7 * sb + ck_b
+
+            def fn():
+                _, _, ck = binding.scan_fwd(g["a"], g["v"], g["q"], mode=wl.mode,
+                                            return_ckpt=True, final_state=eT, y=y)
+                binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], ckpt=ck, mode=wl.mode)
+        else:
+            nbytes = nelem * 4 * sb + B * H * Dh * 4
+
+            def fn():
+                binding.scan_fwd(g["a"], g["v"], g["q"], mode=wl.mode, final_state=eT, y=y)
+        ms = gpu_ms(fn)
+        cold_ms = gpu_ms_cold(fn) if nbytes < (512 << 20) else None
+        mode = 0 if wl.mode == "direct" else 1
+        T_s = min(T, 8192)
+        n_thr = min(B, args.cpu_threads)
+        rec = {"workload": name, "B": B, "T": T, "H": H, "Dh": Dh, "dtype": wl.dtype,
+               "mode": wl.mode, "path": "fwd+bwd" if bwd else "fwd", "gpu_ms": round(ms, 5),
+               "gpu_tokens_per_s": B * T / (ms * 1e-3),
+               "algorithmic_GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if cold_ms is not None:  # small enough to stay cache-resident between launches
+            rec["gpu_ms_cache_flushed"] = round(cold_ms, 5)
+        if not args.no_cpu_baseline:
+            rec["oracle_sample"] = f"rows x T={T_s}: 1 row on 1 thread, {n_thr} rows on {n_thr}"
+            rec["oracle_tokens_per_s_1thread"] = oracle_rate(g, mode, 1, T_s, 1, bwd)
+            rec["oracle_tokens_per_s_nthreads"] = oracle_rate(g, mode, n_thr, T_s, n_thr, bwd)
+            rec["oracle_threads"] = n_thr
+        out.append(rec)
+        del g, y, eT
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:  # the oracle's one-token update on the decode batch
+        wl = synth.WORKLOADS["decode_f16"]
+        s = {k: oracle._f64(t) for k, t in synth.decode_step_inputs(wl, 0).items()}
+        st = oracle._f64(synth.random_state(wl.B, wl.H, wl.Dh, 1))
+        n = 20
+        t0 = time.perf_counter()
+        for _ in range(n):
+            _, st = oracle.state_step(s["a"], s["v"], s["q"], st, mode=1)
+        out.append({"workload": "decode_f16", "path": "step", "B": wl.B,
+                    "oracle_steps_per_s_1thread": n / (time.perf_counter() - t0)})
+    return out
+
+
 def bench_copy(args, torch):
     """A plain device-to-device copy of 4 GiB: reads and writes exactly 4 GiB each, the
     reference that scales the HBM traffic counters (FETCH_SIZE, WRITE_SIZE)."""
