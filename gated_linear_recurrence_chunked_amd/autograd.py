@@ -27,9 +27,11 @@ from . import binding
 
 class _ScanFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, a, v, q, init_state, mode):
-        y, final_state, ckpt = binding.scan_fwd(a, v, q, init_state, mode=mode, return_ckpt=True)
+    def forward(ctx, a, v, q, init_state, mode, deterministic):
+        y, final_state, ckpt = binding.scan_fwd(a, v, q, init_state, mode=mode, return_ckpt=True,
+                                                deterministic=deterministic)
         ctx.mode = mode
+        ctx.deterministic = deterministic
         ctx.has_init = init_state is not None
         ctx.save_for_backward(a, v, q, init_state if init_state is not None else a.new_empty(0),
                               ckpt)
@@ -43,13 +45,15 @@ class _ScanFn(torch.autograd.Function):
             dy = torch.zeros_like(a)
         da, dv, dq, d_init = binding.scan_bwd(a, v, q, dy.contiguous(), init_state,
                                               None if d_final is None else d_final.contiguous(),
-                                              ckpt=ckpt, mode=ctx.mode)
-        return da, dv, dq, (d_init if ctx.has_init else None), None
+                                              ckpt=ckpt, mode=ctx.mode,
+                                              deterministic=ctx.deterministic)
+        return da, dv, dq, (d_init if ctx.has_init else None), None, None
 
 
-def esa_scan(a, v, q, init_state=None, mode="controlled"):
-    """Differentiable scan: returns (y [B,T,H,Dh], final_state fp32 [B,H,Dh])."""
-    return _ScanFn.apply(a, v, q, init_state, mode)
+def esa_scan(a, v, q, init_state=None, mode="controlled", deterministic=False):
+    """Differentiable scan: returns (y [B,T,H,Dh], final_state fp32 [B,H,Dh]).
+    deterministic=True: bitwise reproducible forward and backward."""
+    return _ScanFn.apply(a, v, q, init_state, mode, deterministic)
 
 
 class ESALayer(torch.nn.Module):

@@ -36,6 +36,7 @@ STATUS_NAMES = {0: "ESA_OK", 1: "ESA_ERR_INVALID_ARG", 2: "ESA_ERR_UNSUPPORTED",
 DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4m3fn: 3,
           torch.float8_e5m2: 4}
 MODES = {"direct": 0, "controlled": 1}
+DETERMINISTIC = 0x100  # ESA_DETERMINISTIC: OR-ed into the mode, bitwise reproducible scans
 
 # every function include/esa.h declares: name -> (restype, argtypes)
 _P = ctypes.c_void_p
@@ -133,10 +134,9 @@ class _OnDevice:
         return False
 
 
-def _mode(mode) -> int:
-    if isinstance(mode, str):
-        return MODES[mode]
-    return int(mode)
+def _mode(mode, deterministic=False) -> int:
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    return m | DETERMINISTIC if deterministic else m
 
 
 def _seq(name, t, like=None):
@@ -194,8 +194,9 @@ def get_workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def scan_fwd(a, v, q, init_state=None, mode="controlled", return_ckpt=False, final_state=None,
-             y=None, workspace=None):
-    """Forward scan with fused gate and readout (esa_scan_fwd)."""
+             y=None, workspace=None, deterministic=False):
+    """Forward scan with fused gate and readout (esa_scan_fwd).  deterministic=True makes the
+    result bitwise reproducible (ESA_DETERMINISTIC)."""
     lib = load_library()
     a = _seq("gate_logit", a)
     v = _seq("value", v, a)
@@ -217,7 +218,8 @@ def scan_fwd(a, v, q, init_state=None, mode="controlled", return_ckpt=False, fin
     need = workspace_bytes(B, T, H, Dh, a.dtype)
     ws = workspace if workspace is not None else get_workspace(need, a.device)
     with _OnDevice(a.device.index):
-        st = lib.esa_scan_fwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode), _ptr(a), _ptr(v), _ptr(q),
+        st = lib.esa_scan_fwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode, deterministic), _ptr(a),
+                              _ptr(v), _ptr(q),
                               _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(ckpt), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream_handle(a.device))
     _check(st, "esa_scan_fwd")
@@ -227,7 +229,7 @@ def scan_fwd(a, v, q, init_state=None, mode="controlled", return_ckpt=False, fin
 
 
 def scan_bwd(a, v, q, dy, init_state=None, d_final_state=None, ckpt=None, mode="controlled",
-             workspace=None):
+             workspace=None, deterministic=False):
     """Backward of scan_fwd (esa_scan_bwd).  Returns (d_logit, d_value, d_query, d_init)."""
     lib = load_library()
     a = _seq("gate_logit", a)
@@ -248,7 +250,8 @@ def scan_bwd(a, v, q, dy, init_state=None, d_final_state=None, ckpt=None, mode="
     need = workspace_bytes(B, T, H, Dh, a.dtype)
     ws = workspace if workspace is not None else get_workspace(need, a.device)
     with _OnDevice(a.device.index):
-        st = lib.esa_scan_bwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode), _ptr(a), _ptr(v), _ptr(q),
+        st = lib.esa_scan_bwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode, deterministic), _ptr(a),
+                              _ptr(v), _ptr(q),
                               _ptr(init_state), _ptr(dy), _ptr(d_final_state), _ptr(ckpt),
                               _ptr(da), _ptr(dv), _ptr(dq), _ptr(d_init), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream_handle(a.device))
@@ -288,7 +291,7 @@ def state_step(a, v, q, state, mode="controlled", y=None):
     return y
 
 
-def segment_fwd(a, v, mode="controlled", workspace=None):
+def segment_fwd(a, v, mode="controlled", workspace=None, deterministic=False):
     """Aggregate of one sequence segment from a zero state (esa_scan_segment_fwd): returns
     (seg_state, seg_gate_prod), fp32 [B, H, Dh] each."""
     lib = load_library()
@@ -300,14 +303,16 @@ def segment_fwd(a, v, mode="controlled", workspace=None):
     need = workspace_bytes(B, T, H, Dh, a.dtype)
     ws = workspace if workspace is not None else get_workspace(need, a.device)
     with _OnDevice(a.device.index):
-        st = lib.esa_scan_segment_fwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode), _ptr(a), _ptr(v),
+        st = lib.esa_scan_segment_fwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode, deterministic),
+                                      _ptr(a), _ptr(v),
                                       _ptr(seg_state), _ptr(seg_prod), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream_handle(a.device))
     _check(st, "esa_scan_segment_fwd")
     return seg_state, seg_prod
 
 
-def segment_bwd(a, v, q, dy, init_state=None, ckpt=None, mode="controlled", workspace=None):
+def segment_bwd(a, v, q, dy, init_state=None, ckpt=None, mode="controlled", workspace=None,
+                deterministic=False):
     """Gradient reaching a segment's initial state with none arriving at its end
     (esa_scan_segment_bwd): fp32 [B, H, Dh]."""
     lib = load_library()
@@ -325,7 +330,8 @@ def segment_bwd(a, v, q, dy, init_state=None, ckpt=None, mode="controlled", work
     need = workspace_bytes(B, T, H, Dh, a.dtype)
     ws = workspace if workspace is not None else get_workspace(need, a.device)
     with _OnDevice(a.device.index):
-        st = lib.esa_scan_segment_bwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode), _ptr(a), _ptr(v),
+        st = lib.esa_scan_segment_bwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode, deterministic),
+                                      _ptr(a), _ptr(v),
                                       _ptr(q), _ptr(init_state), _ptr(dy), _ptr(ckpt),
                                       _ptr(seg_d_init), _ptr(ws), ws.numel() * ws.element_size(),
                                       _stream_handle(a.device))

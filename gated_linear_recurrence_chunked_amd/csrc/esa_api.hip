@@ -17,7 +17,8 @@ namespace {
 
 struct Problem {
     int64_t B, T, H, Dh, C, nLanes, nElem;
-    int dtype, mode;
+    int dtype, mode;  // mode: the recurrence form (ESA_DIRECT / ESA_CONTROLLED)
+    uint32_t det;     // ESA_DETERMINISTIC was set
     int64_t esize;
 };
 
@@ -68,7 +69,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int check_sizes(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode, Problem* pr) {
-    if (dtype < ESA_F32 || dtype > ESA_F8E5M2 || mode < ESA_DIRECT || mode > ESA_CONTROLLED)
+    const int form = mode & ~ESA_DETERMINISTIC;
+    if (dtype < ESA_F32 || dtype > ESA_F8E5M2 || form < ESA_DIRECT || form > ESA_CONTROLLED)
         return ESA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || Dh < 1 || T < 0) return ESA_ERR_INVALID_ARG;
     if (!supported_dh(Dh)) return ESA_ERR_UNSUPPORTED;
@@ -77,7 +79,8 @@ int check_sizes(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode
     pr->H = H;
     pr->Dh = Dh;
     pr->dtype = dtype;
-    pr->mode = mode;
+    pr->mode = form;
+    pr->det = (mode & ESA_DETERMINISTIC) ? 1u : 0u;
     pr->esize = storage_bytes(dtype);
     int64_t bytes;
     if (!mul64(H, Dh, &pr->C) || !mul64(B, pr->C, &pr->nLanes) || !mul64(pr->nLanes, T, &pr->nElem) ||
@@ -267,9 +270,10 @@ int scan_bwd_impl(bool grads, int64_t B, int64_t T, int64_t H, int64_t Dh, int d
         f.nck = L.nck;
         f.nCB = L.nCB;
         f.nTiles = L.nTilesF;
+        f.det = pr.det;
         rc = set_epoch(s, hdr, &f.epoch, &f.epochWord);
         if (rc != ESA_OK) return rc;
-        rc = hip_status(ESA_DISPATCH(fwd, dtype, mode, Dh, f, s));
+        rc = hip_status(ESA_DISPATCH(fwd, dtype, pr.mode, Dh, f, s));
         if (rc != ESA_OK) return rc;
         ck = f.ckpt;
     }
@@ -294,9 +298,10 @@ int scan_bwd_impl(bool grads, int64_t B, int64_t T, int64_t H, int64_t Dh, int d
     p.nck = L.nck;
     p.nCB = L.nCB;
     p.nTiles = L.nTilesB;
+    p.det = pr.det;
     rc = set_epoch(s, hdr, &p.epoch, &p.epochWord);
     if (rc != ESA_OK) return rc;
-    return hip_status(ESA_DISPATCH(bwd, dtype, mode, Dh, p, s));
+    return hip_status(ESA_DISPATCH(bwd, dtype, pr.mode, Dh, p, s));
 }
 
 }  // namespace
@@ -385,9 +390,10 @@ int esa_scan_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mod
     p.nck = L.nck;
     p.nCB = L.nCB;
     p.nTiles = L.nTilesF;
+    p.det = pr.det;
     rc = set_epoch(s, p.hdr, &p.epoch, &p.epochWord);
     if (rc != ESA_OK) return rc;
-    return hip_status(ESA_DISPATCH(fwd, dtype, mode, Dh, p, s));
+    return hip_status(ESA_DISPATCH(fwd, dtype, pr.mode, Dh, p, s));
 }
 
 int esa_scan_bwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
@@ -420,7 +426,7 @@ int esa_state_step(int64_t B, int64_t H, int64_t Dh, int dtype, int mode, const 
     p.state = state;
     p.y = y;
     p.nLanes = pr.nLanes;
-    return hip_status(ESA_DISPATCH(step, dtype, mode, Dh, p, (hipStream_t)stream));
+    return hip_status(ESA_DISPATCH(step, dtype, pr.mode, Dh, p, (hipStream_t)stream));
 }
 
 int esa_scan_segment_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
@@ -466,9 +472,10 @@ int esa_scan_segment_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype,
     f.nck = L.nck;
     f.nCB = L.nCB;
     f.nTiles = L.nTilesF;
+    f.det = pr.det;
     rc = set_epoch(s, f.hdr, &f.epoch, &f.epochWord);
     if (rc != ESA_OK) return rc;
-    return hip_status(ESA_DISPATCH(fwd, dtype, mode, Dh, f, s));
+    return hip_status(ESA_DISPATCH(fwd, dtype, pr.mode, Dh, f, s));
 }
 
 int esa_scan_segment_bwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,

@@ -217,7 +217,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
             } else {
                 float pin;  // unused: the backward carries no gate product
                 carry = chain_carry(p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc,
-                                    p.hdr, tp, te, &pin);
+                                    p.hdr, tp, te, &pin, p.det != 0);
             }
             const float lam_out = te + tp * carry;
             publish(X, tagInc, lam_out);

@@ -170,6 +170,7 @@ struct FwdParams {
     uint32_t nTiles;
     uint32_t epoch;  // tags of this call's look-back words (host epoch)
     const uint32_t* epochWord;  // non-NULL: read the epoch here instead (graph-recorded launch)
+    uint32_t det;    // non-zero: every tile waits for its neighbour's inclusive value
 };
 
 struct BwdParams {
@@ -195,6 +196,7 @@ struct BwdParams {
     uint32_t nTiles;
     uint32_t epoch;
     const uint32_t* epochWord;
+    uint32_t det;
 };
 
 struct StepParams {
@@ -557,6 +559,21 @@ __device__ __forceinline__ float word_val(uint64_t w) {
 // through the tile before `tile` (NaN when the wait gave up).
 constexpr uint32_t kSpinLimit = 1u << 20;
 
+// One unproductive poll of a bounded wait: false once the wait must give up (the workspace's
+// abort word is set, or this wait has polled kSpinLimit times; then it sets the abort word).
+__device__ __forceinline__ bool wait_turn(uint32_t polls, uint32_t* hdr) {
+    if ((polls & 255u) == 0u) {
+        const bool abort =
+            __hip_atomic_load(&hdr[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+        if (abort || polls >= kSpinLimit) {
+            if (!abort) __hip_atomic_store(&hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+    }
+    __builtin_amdgcn_s_sleep(1);
+    return true;
+}
+
 template <bool PROD = false>
 __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t* flagY,
                                            int64_t nLanes, int64_t lane, int64_t tile, int step,
@@ -587,17 +604,10 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
                 continue;
             }
         }
-        ++polls;
-        if ((polls & 255u) == 0u) {
-            const bool abort =
-                __hip_atomic_load(&hdr[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-            if (abort || polls >= kSpinLimit) {
-                if (!abort) __hip_atomic_store(&hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if constexpr (PROD) *pinc = __builtin_nanf("");
-                return __builtin_nanf("");
-            }
+        if (!wait_turn(++polls, hdr)) {
+            if constexpr (PROD) *pinc = __builtin_nanf("");
+            return __builtin_nanf("");
         }
-        __builtin_amdgcn_s_sleep(1);
     }
 }
 
@@ -609,12 +619,35 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
 // aggregate pair (te, tp) and walks back.  The caller then publishes the inclusive value.
 // Successors cope with a tile that never publishes an aggregate: they wait for its
 // inclusive word, which follows without any wait of its own.
+//
+// With `det` the tile always waits for its neighbour's inclusive value: every carry is then
+// the same fp32 expression on every run (bitwise reproducible results), at the price of
+// resolving a chain's tiles one after another (free when a chain has about one tile
+// resident at a time, as at 64K context; ~10x slower for a single long chain).
 template <bool PROD = false>
 __device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, int64_t nLanes,
                                              int64_t lane, int64_t tile, int step, uint32_t tagAgg,
                                              uint32_t tagInc, uint32_t* hdr, float tp, float te,
-                                             float* pin) {
+                                             float* pin, bool det) {
     const int64_t nb = (tile + step) * nLanes + lane;
+    if (det) {
+        uint32_t polls = 0;
+        for (;;) {
+            const uint64_t x = peek(flagX + nb);
+            if (word_tag(x) == tagInc) {
+                if constexpr (!PROD) return word_val(x);
+                const uint64_t y = peek(flagY + nb);
+                if (word_tag(y) == tagInc) {
+                    *pin = word_val(y);
+                    return word_val(x);
+                }
+            }
+            if (!wait_turn(++polls, hdr)) {
+                if constexpr (PROD) *pin = __builtin_nanf("");
+                return __builtin_nanf("");
+            }
+        }
+    }
     const uint64_t x = peek(flagX + nb);
     if (word_tag(x) == tagInc) {
         if constexpr (!PROD) return word_val(x);

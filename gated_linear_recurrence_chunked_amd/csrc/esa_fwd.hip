@@ -120,7 +120,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
                 carry = p.e0 ? p.e0[gl] : 0.0f;
             } else {
                 carry = chain_carry<PROD>(p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg,
-                                          tagInc, p.hdr, tp, te, &pin);
+                                          tagInc, p.hdr, tp, te, &pin, p.det != 0);
             }
             if constexpr (PROD) {
                 publish(Y, tagInc, tp * pin);

@@ -56,8 +56,8 @@
 extern "C" {
 #endif
 
-/* 1: fp32 / fp16 / bf16 storage.  2: adds the fp8 storage dtypes ESA_F8E4M3, ESA_F8E5M2
- * and the sequence-segment calls. */
+/* 1: fp32 / fp16 / bf16 storage.  2: adds the fp8 storage dtypes ESA_F8E4M3, ESA_F8E5M2,
+ * the sequence-segment calls and the ESA_DETERMINISTIC mode flag. */
 #define ESA_ABI_VERSION 2
 
 /* Checkpoint granularity: the forward can store the fp32 state at every 64th step. */
@@ -86,6 +86,15 @@ typedef enum {
 
 /* Recurrence form (page "entangled-state-attention 0.1.0", "Direct vs controlled mode"). */
 typedef enum { ESA_DIRECT = 0, ESA_CONTROLLED = 1 } esa_mode;
+
+/* Flag OR-ed into the mode argument of the scan calls: bitwise reproducible results.  Every
+ * tile then waits for the inclusive value of the tile before it, so each carry is the same
+ * fp32 expression on every run; without the flag a tile may combine whatever earlier
+ * tiles have published, so the last bits can differ from run to run (always within the
+ * parity bar).  The cost is serialising each chain of tiles: about nothing when a chain has
+ * about one tile in flight (B*H*Dh >= 32K lanes at long T, e.g. the 64K-context workload),
+ * up to ~10x for a single long chain (B*H*Dh = 64).  esa_state_step accepts and ignores it. */
+#define ESA_DETERMINISTIC 0x100
 
 /* ABI version of the loaded library (ESA_ABI_VERSION at build time). */
 int esa_abi_version(void);

@@ -100,6 +100,9 @@ def test_fwd_validation(lib):
     assert fwd(lib, B=0) == INVALID
     assert fwd(lib, T=-1) == INVALID
     assert fwd(lib, dt=5) == INVALID
+    assert fwd(lib, mode=0x102) == INVALID  # deterministic flag with a bad form
+    assert fwd(lib, mode=0x200) == INVALID  # unknown flag
+    assert fwd(lib, mode=0x101, y=1) == INVALID  # a valid flagged mode still validates the rest
     assert fwd(lib, dt=-1) == INVALID
     assert fwd(lib, mode=2) == INVALID
     assert fwd(lib, Dh=48) == UNSUPPORTED

@@ -105,3 +105,40 @@ def test_repeated_runs_agree():
         assert_close("y", y, outs[0][0], torch.float32)
         assert_close("eT", eT, outs[0][1], torch.float32)
     check_abort_clear()
+
+
+@pytest.mark.parametrize("dt,mode", [(torch.float16, "controlled"), (torch.float32, "direct")])
+def test_deterministic_flag_gives_bitwise_identical_runs(dt, mode):
+    """ESA_DETERMINISTIC: every run of the forward, the backward and the segment pass gives
+    the same bits, on a shape whose two chains have many tiles in flight at once (where the
+    default look-back combines whatever is published and may differ in the last bits)."""
+    B, T, H, Dh = 1, 20000, 2, 64
+    say(f"deterministic {dt} {mode}")
+    shp = (B, T, H, Dh)
+    x = {k: synth.normal(shp, 920 + i, 1.0 if k == "a" else 0.0, 1.5 if k == "a" else 1.0, dt)
+         for i, k in enumerate(("a", "v", "q", "dy"))}
+    e0 = synth.random_state(B, H, Dh, 925)
+    g = {k: t.to(DEV) for k, t in x.items()}
+    ge0 = e0.to(DEV)
+    runs = []
+    for _ in range(4):
+        y, eT, ck = binding.scan_fwd(g["a"], g["v"], g["q"], ge0, mode=mode, return_ckpt=True,
+                                     deterministic=True)
+        grads = binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], ge0, None, ckpt=ck, mode=mode,
+                                 deterministic=True)
+        seg = binding.segment_fwd(g["a"], g["v"], mode=mode, deterministic=True)
+        runs.append((y, eT, ck) + tuple(grads) + tuple(seg))
+    torch.cuda.synchronize()
+    check_abort_clear()
+    for r in runs[1:]:
+        for got, ref in zip(r, runs[0]):
+            assert torch.equal(got, ref)
+    m = 0 if mode == "direct" else 1
+    ry, reT = oracle.scan_fwd(x["a"], x["v"], x["q"], e0, mode=m)
+    rda, rdv, rdq, rde0 = oracle.scan_bwd(x["a"], x["v"], x["q"], x["dy"], e0, None, mode=m)
+    y, eT, _, da, dv, dq, de0, _, _ = runs[0]
+    assert_close("y", y, ry, dt)
+    assert_close("eT", eT, reT, dt)
+    for name, got, ref in (("d_logit", da, rda), ("d_value", dv, rdv), ("d_query", dq, rdq),
+                           ("d_init", de0, rde0)):
+        assert_close(name, got, ref, dt)
