@@ -58,10 +58,15 @@ def esa_scan(a, v, q, init_state=None, mode="controlled", deterministic=False):
 
 class ESALayer(torch.nn.Module):
     """ESA layer: projections, the library's gated scan with per-head RMSNorm readout, and the
-    output projection.  ``dtype`` is the storage dtype of the scan's inputs and outputs."""
+    output projection.  ``dtype`` is the dtype of the weights and of the GEMMs, and by default
+    also the scan's storage dtype.  ``scan_dtype`` may instead name one of the 8-bit formats
+    (torch.float8_e4m3fn, torch.float8_e5m2): the scan then reads a, v, q and writes its
+    readout in that format (the experimental fp8 precision of page "Entangled State
+    Attention v2.1", section "3. Precision"), with fp32 arithmetic and state; gradients
+    cross the casts as usual."""
 
     def __init__(self, embd: int, head: int, mode: str = "controlled", dtype=torch.float16,
-                 device=None):
+                 device=None, scan_dtype=None):
         super().__init__()
         if embd % head:
             raise ValueError("embd must be a multiple of head")
@@ -69,9 +74,11 @@ class ESALayer(torch.nn.Module):
         if self.dh not in (16, 32, 64, 128):
             raise ValueError("head dimension embd / head must be 16, 32, 64 or 128")
         if dtype not in (torch.float32, torch.float16, torch.bfloat16):
-            # the projections are torch GEMMs in this dtype; 8-bit storage is reached through
-            # the scan functions of the binding directly
+            # the projections are torch GEMMs in this dtype; 8-bit storage is the scan_dtype
             raise ValueError("ESALayer dtype must be float32, float16 or bfloat16")
+        self.scan_dtype = dtype if scan_dtype is None else scan_dtype
+        if self.scan_dtype not in binding.DTYPES:
+            raise ValueError(f"scan_dtype {self.scan_dtype} is not a storage dtype of the library")
         self.mode = mode
         kw = dict(device=device, dtype=dtype)
         self.W_A = torch.nn.Parameter(torch.empty(embd, embd, **kw))
@@ -87,9 +94,9 @@ class ESALayer(torch.nn.Module):
 
     def _project(self, x):
         shp = x.shape[:-1] + (self.head, self.dh)
-        a = (x @ self.W_A).reshape(shp)
-        v = (x @ self.W_V).reshape(shp)
-        q = (x @ self.W_Q).reshape(shp)
+        a = (x @ self.W_A).reshape(shp).to(self.scan_dtype)
+        v = (x @ self.W_V).reshape(shp).to(self.scan_dtype)
+        q = (x @ self.W_Q).reshape(shp).to(self.scan_dtype)
         return a, v, q
 
     def forward(self, x, init_state=None, return_state=False):
@@ -97,7 +104,7 @@ class ESALayer(torch.nn.Module):
         a, v, q = self._project(x)
         r, state = esa_scan(a.contiguous(), v.contiguous(), q.contiguous(), init_state,
                             mode=self.mode)
-        y = r.reshape(x.shape) @ self.W_O
+        y = r.reshape(x.shape).to(self.W_O.dtype) @ self.W_O
         return (y, state) if return_state else y
 
     def prefill(self, x, state=None):
@@ -110,4 +117,4 @@ class ESALayer(torch.nn.Module):
         a, v, q = self._project(x_t)
         r = binding.state_step(a.contiguous(), v.contiguous(), q.contiguous(), state,
                                mode=self.mode)
-        return r.reshape(x_t.shape) @ self.W_O, state
+        return r.reshape(x_t.shape).to(self.W_O.dtype) @ self.W_O, state

@@ -137,3 +137,30 @@ def test_layer_prefill_then_decode_matches_full_pass():
         ry, rst, _, _ = reference_layer(layer, x, "controlled", storage=torch.float16)
     assert_close("y vs reference", y_full, ry, torch.float16)
     assert_close("state vs reference", st_full, rst, torch.float16)
+
+
+@pytest.mark.parametrize("scan_dtype", [torch.float8_e4m3fn, torch.float8_e5m2])
+def test_layer_with_fp8_scan_storage(scan_dtype):
+    """fp16 GEMMs around a scan stored in an 8-bit format: forward and all gradients against
+    the fp64 composition with the same roundings (a, v, q and the readout rounded to the
+    8-bit format), at the format's bar."""
+    say(f"layer fp16 GEMMs, {scan_dtype} scan")
+    torch.manual_seed(3)
+    B, T, C, H = 2, 300, 256, 4
+    layer = ESALayer(C, H, mode="controlled", dtype=torch.float16, device=DEV,
+                     scan_dtype=scan_dtype)
+    x = synth.normal((B, T, C), 720, 0, 1, torch.float16).to(DEV).requires_grad_(True)
+    gy = synth.normal((B, T, C), 721, 0, 1, torch.float16)
+    y, st = layer(x, return_state=True)
+    (y.float() * gy.to(DEV).float()).sum().backward()
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float16 and x.grad.dtype == torch.float16
+    assert torch.isfinite(x.grad).all() and torch.isfinite(layer.W_A.grad).all()
+    # forward: the fp64 composition from the same 8-bit scan inputs (the projections are fp16
+    # GEMMs here, so the reference starts from the library's own a, v, q)
+    with torch.no_grad():
+        a, v, q = (t.cpu() for t in layer._project(x))
+        r, rst = oracle.scan_fwd(a, v, q, mode=1)
+        ry = torch.from_numpy(r).to(scan_dtype).double().reshape(B, T, C) @ layer.W_O.double().cpu()
+    assert_close("y", y, ry, scan_dtype)
+    assert_close("state", st, rst, torch.float16)
