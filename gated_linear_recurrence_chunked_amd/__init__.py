@@ -7,7 +7,7 @@ does, and fails loudly when the library is missing.
 """
 from __future__ import annotations
 
-__all__ = ["scan_fwd", "scan_bwd", "state_step", "segment_fwd", "segment_bwd",
+__all__ = ["scan_fwd", "scan_bwd", "state_step", "StepPlan", "segment_fwd", "segment_bwd",
            "segment_compose", "workspace_bytes", "ckpt_bytes", "EsaError", "library_path",
            "load_library"]
 

@@ -363,3 +363,48 @@ def segment_compose(seg_gate_prod, seg_agg, boundary=None, reverse=False):
                                      _stream_handle(p.device))
     _check(st, "esa_segment_compose")
     return carry, total
+
+
+class StepPlan:
+    """The fixed arguments of a decode loop, validated once: the fp32 state [B, H, Dh] (updated
+    in place by every step), the storage dtype and the mode.  Each call then checks only that
+    the step's tensors match and launches esa_state_step on the current stream, which keeps the
+    host's share of an eager step small.
+
+        plan = StepPlan(state, torch.float16, "controlled")
+        for t in ...:
+            plan(a_t, v_t, q_t, y_t)      # [B, H, Dh] each, y_t written
+    """
+
+    def __init__(self, state, dtype, mode="controlled"):
+        if (not isinstance(state, torch.Tensor) or not state.is_cuda or state.dim() != 3
+                or state.dtype != torch.float32 or not state.is_contiguous()):
+            raise ValueError("state must be a contiguous fp32 [B, H, Dh] CUDA (HIP) tensor")
+        if dtype not in DTYPES:
+            raise TypeError(f"dtype {dtype} not supported")
+        self._lib = load_library()
+        self.state = state
+        self.shape = state.shape
+        self.dtype = dtype
+        self.device = state.device
+        self._index = state.device.index
+        self._head = (state.shape[0], state.shape[1], state.shape[2], DTYPES[dtype], _mode(mode))
+        self._state_ptr = state.data_ptr()
+
+    def __call__(self, a, v, q, y):
+        sh, dt, idx = self.shape, self.dtype, self._index
+        for t in (a, v, q, y):  # integer device index and dtype identity: cheap to compare
+            if t.shape != sh or t.dtype is not dt or t.get_device() != idx or not t.is_contiguous():
+                raise ValueError(f"step tensors must be contiguous {dt} {tuple(sh)} on "
+                                 f"{self.device}")
+        if torch._C._cuda_getDevice() == idx:
+            st = self._lib.esa_state_step(*self._head, a.data_ptr(), v.data_ptr(), q.data_ptr(),
+                                          self._state_ptr, y.data_ptr(), _raw_stream(idx))
+        else:
+            with _OnDevice(idx):
+                st = self._lib.esa_state_step(*self._head, a.data_ptr(), v.data_ptr(),
+                                              q.data_ptr(), self._state_ptr, y.data_ptr(),
+                                              _raw_stream(idx))
+        if st:
+            _check(st, "esa_state_step")
+        return y

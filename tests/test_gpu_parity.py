@@ -151,6 +151,32 @@ def test_step_parity(dt, Dh, mode):
     assert_close("state", st, rst, state_bar(dtype))
 
 
+def test_step_plan_matches_oracle_and_checks_its_tensors():
+    """binding.StepPlan: the decode loop's fixed arguments validated once; steps through it
+    equal the oracle's state_step chain, and a mismatched step tensor is refused."""
+    say("step plan")
+    B, H, Dh = 6, 2, 64
+    st0 = synth.random_state(B, H, Dh, seed=21)
+    st = st0.to(DEV)
+    plan = binding.StepPlan(st, torch.float16, "controlled")
+    rst = st0
+    for k in range(5):
+        x = inputs_cpu(B, 1, H, Dh, torch.float16, seed=300 + k)
+        a, v, q = (x[n][:, 0].contiguous() for n in ("a", "v", "q"))
+        y = torch.empty((B, H, Dh), dtype=torch.float16, device=DEV)
+        plan(a.to(DEV), v.to(DEV), q.to(DEV), y)
+        torch.cuda.synchronize()
+        ry, rst = oracle.state_step(a, v, q, rst, mode=1)
+        assert_close(f"y step {k}", y, ry, torch.float16)
+        assert_close(f"state step {k}", st, rst, torch.float16)
+    good = torch.empty((B, H, Dh), dtype=torch.float16, device=DEV)
+    for bad in (torch.empty((B, H, Dh), dtype=torch.bfloat16, device=DEV),
+                torch.empty((B, H, Dh + 1), dtype=torch.float16, device=DEV),
+                torch.empty((B, H, 2 * Dh), dtype=torch.float16, device=DEV)[..., ::2]):
+        with pytest.raises(ValueError):
+            plan(good, good, good, bad)
+
+
 def test_empty_sequence():
     say("empty sequence")
     B, H, Dh = 2, 2, 32
