@@ -63,16 +63,20 @@ class ESALayer(torch.nn.Module):
     (torch.float8_e4m3fn, torch.float8_e5m2): the scan then reads a, v, q and writes its
     readout in that format (the experimental fp8 precision of page "Entangled State
     Attention v2.1", section "3. Precision"), with fp32 arithmetic and state; gradients
-    cross the casts as usual."""
+    cross the casts as usual.  ``state_dim`` (default ``embd``) is the width of the
+    recurrent state, split over the heads, as the ``ESA(dim, state_dim, gate_mode)`` layer of
+    page "entangled-state-attention 0.1.0", section "Minimal usage": W_A, W_V, W_Q map embd to
+    state_dim and W_O maps it back."""
 
     def __init__(self, embd: int, head: int, mode: str = "controlled", dtype=torch.float16,
-                 device=None, scan_dtype=None):
+                 device=None, scan_dtype=None, state_dim: int | None = None):
         super().__init__()
-        if embd % head:
-            raise ValueError("embd must be a multiple of head")
-        self.embd, self.head, self.dh = embd, head, embd // head
+        state_dim = embd if state_dim is None else state_dim
+        if state_dim % head:
+            raise ValueError("state_dim (default embd) must be a multiple of head")
+        self.embd, self.head, self.state_dim, self.dh = embd, head, state_dim, state_dim // head
         if self.dh not in (16, 32, 64, 128):
-            raise ValueError("head dimension embd / head must be 16, 32, 64 or 128")
+            raise ValueError("head dimension state_dim / head must be 16, 32, 64 or 128")
         if dtype not in (torch.float32, torch.float16, torch.bfloat16):
             # the projections are torch GEMMs in this dtype; 8-bit storage is the scan_dtype
             raise ValueError("ESALayer dtype must be float32, float16 or bfloat16")
@@ -81,15 +85,15 @@ class ESALayer(torch.nn.Module):
             raise ValueError(f"scan_dtype {self.scan_dtype} is not a storage dtype of the library")
         self.mode = mode
         kw = dict(device=device, dtype=dtype)
-        self.W_A = torch.nn.Parameter(torch.empty(embd, embd, **kw))
-        self.W_V = torch.nn.Parameter(torch.empty(embd, embd, **kw))
-        self.W_Q = torch.nn.Parameter(torch.empty(embd, embd, **kw))
-        self.W_O = torch.nn.Parameter(torch.empty(embd, embd, **kw))
+        self.W_A = torch.nn.Parameter(torch.empty(embd, state_dim, **kw))
+        self.W_V = torch.nn.Parameter(torch.empty(embd, state_dim, **kw))
+        self.W_Q = torch.nn.Parameter(torch.empty(embd, state_dim, **kw))
+        self.W_O = torch.nn.Parameter(torch.empty(state_dim, embd, **kw))
         self.reset_parameters()
 
     def reset_parameters(self):
-        bound = 1.0 / math.sqrt(self.embd)
         for w in (self.W_A, self.W_V, self.W_Q, self.W_O):
+            bound = 1.0 / math.sqrt(w.shape[0])  # fan-in
             torch.nn.init.uniform_(w, -bound, bound)
 
     def _project(self, x):
@@ -100,11 +104,11 @@ class ESALayer(torch.nn.Module):
         return a, v, q
 
     def forward(self, x, init_state=None, return_state=False):
-        """x: [B, T, embd] -> y [B, T, embd] (and the fp32 state [B, head, dh])."""
+        """x: [B, T, embd] -> y [B, T, embd] (and the fp32 state [B, head, state_dim/head])."""
         a, v, q = self._project(x)
         r, state = esa_scan(a.contiguous(), v.contiguous(), q.contiguous(), init_state,
                             mode=self.mode)
-        y = r.reshape(x.shape).to(self.W_O.dtype) @ self.W_O
+        y = r.reshape(x.shape[:-1] + (self.state_dim,)).to(self.W_O.dtype) @ self.W_O
         return (y, state) if return_state else y
 
     def prefill(self, x, state=None):
@@ -117,4 +121,4 @@ class ESALayer(torch.nn.Module):
         a, v, q = self._project(x_t)
         r = binding.state_step(a.contiguous(), v.contiguous(), q.contiguous(), state,
                                mode=self.mode)
-        return r.reshape(x_t.shape).to(self.W_O.dtype) @ self.W_O, state
+        return r.reshape(x_t.shape[:-1] + (self.state_dim,)).to(self.W_O.dtype) @ self.W_O, state

@@ -83,11 +83,12 @@ def reference_layer(layer, x, mode, e0=None, storage=None):
     xr = x.detach().double().cpu().requires_grad_(True)
     B, T, C = xr.shape
     shp = (B, T, layer.head, layer.dh)
+    S = layer.state_dim
     a = rnd((xr @ W["W_A"]).reshape(shp))
     v = rnd((xr @ W["W_V"]).reshape(shp))
     q = rnd((xr @ W["W_Q"]).reshape(shp))
     r, st = OracleScan.apply(a.contiguous(), v.contiguous(), q.contiguous(), e0, mode)
-    y = rnd(r).reshape(B, T, C) @ W["W_O"]
+    y = rnd(r).reshape(B, T, S) @ W["W_O"]
     return y, st, xr, W
 
 
@@ -164,3 +165,27 @@ def test_layer_with_fp8_scan_storage(scan_dtype):
         ry = torch.from_numpy(r).to(scan_dtype).double().reshape(B, T, C) @ layer.W_O.double().cpu()
     assert_close("y", y, ry, scan_dtype)
     assert_close("state", st, rst, torch.float16)
+
+
+def test_layer_with_state_dim_different_from_embd():
+    """ESA(dim, state_dim) of page "entangled-state-attention 0.1.0", "Minimal usage": the
+    state is wider than the model (embd 96, state 256 over 4 heads of 64); forward and every
+    gradient against the fp64 composition, fp32 throughout."""
+    say("layer state_dim != embd")
+    torch.manual_seed(4)
+    B, T, C, S, H = 2, 200, 96, 256, 4
+    layer = ESALayer(C, H, mode="direct", dtype=torch.float32, device=DEV, state_dim=S)
+    assert layer.W_A.shape == (C, S) and layer.W_O.shape == (S, C)
+    x = synth.normal((B, T, C), 730, 0, 1, torch.float32).to(DEV).requires_grad_(True)
+    gy = synth.normal((B, T, C), 731, 0, 1, torch.float32)
+    y, st = layer(x, return_state=True)
+    (y * gy.to(DEV)).sum().backward()
+    torch.cuda.synchronize()
+    assert y.shape == (B, T, C) and st.shape == (B, H, S // H)
+    ry, rst, xr, W = reference_layer(layer, x, "direct")
+    (ry * gy.double()).sum().backward()
+    assert_close("y", y, ry, torch.float32)
+    assert_close("state", st, rst, torch.float32)
+    assert_close("dx", x.grad, xr.grad, torch.float32)
+    for k in ("W_A", "W_V", "W_Q", "W_O"):
+        assert_close(k, getattr(layer, k).grad, W[k].grad, torch.float32)
