@@ -484,9 +484,10 @@ def main():
     args.cpu_threads = args.cpu_threads or min(16, os.cpu_count() or 1)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU figures "
-                                   "are not part of this build (see the sharding note in the "
-                                   "design notes)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: every lane is "
+                                   "independent, so several GPUs would each run the one-GPU "
+                                   "kernels on their share of the batch or heads",
+                          "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
