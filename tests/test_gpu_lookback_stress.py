@@ -142,3 +142,48 @@ def test_deterministic_flag_gives_bitwise_identical_runs(dt, mode):
     for name, got, ref in (("d_logit", da, rda), ("d_value", dv, rdv), ("d_query", dq, rdq),
                            ("d_init", de0, rde0)):
         assert_close(name, got, ref, dt)
+
+
+def test_concurrent_streams_with_their_own_workspaces():
+    """Scans of three problems on three streams at once, each stream with its own workspace
+    (the binding keeps one per stream), give the same bits as the same calls run one after
+    another on one stream.  Concurrent dispatches share the CUs; each scan's waits are on
+    lower-numbered workgroups of its own dispatch, so neither can block the other."""
+    B, T, H, Dh = 2, 30000, 2, 64
+    dt, mode = torch.float16, "controlled"
+    say("concurrent streams")
+    shp = (B, T, H, Dh)
+    probs = []
+    for p in range(3):
+        x = {k: synth.normal(shp, 940 + 10 * p + i, 1.5 if k == "a" else 0.0, 1.0, dt).to(DEV)
+             for i, k in enumerate(("a", "v", "q", "dy"))}
+        x["e0"] = synth.random_state(B, H, Dh, 945 + 10 * p).to(DEV)
+        probs.append(x)
+
+    def run(x):
+        y, eT, ck = binding.scan_fwd(x["a"], x["v"], x["q"], x["e0"], mode=mode,
+                                     return_ckpt=True, deterministic=True)
+        grads = binding.scan_bwd(x["a"], x["v"], x["q"], x["dy"], x["e0"], None, ckpt=ck,
+                                 mode=mode, deterministic=True)
+        return (y, eT) + tuple(grads)
+
+    ref = [run(x) for x in probs]
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream() for _ in probs]
+    got = []
+    for s, x in zip(streams, probs):
+        s.wait_stream(main)
+        with torch.cuda.stream(s):
+            got.append(run(x))
+    for s in streams:
+        main.wait_stream(s)
+    torch.cuda.synchronize()
+    check_abort_clear()
+    for g, r in zip(got, ref):
+        for a_, b_ in zip(g, r):
+            assert torch.equal(a_, b_)
+    c = {k: t.cpu() for k, t in probs[1].items()}
+    ry, reT = oracle.scan_fwd(c["a"], c["v"], c["q"], c["e0"], mode=1)
+    assert_close("y", got[1][0], ry, dt)
+    assert_close("eT", got[1][1], reT, dt)
