@@ -109,11 +109,11 @@ struct Geom {
 // Per-(dtype, Dh) launch configuration of the forward and backward scans.
 // The forward runs 512-thread workgroups (8 waves): at 64K context a tile is then 256 steps,
 // which halves the look-back words per byte of data against 256 threads and measured ~7 %
-// faster.  The backward holds more per thread (231 VGPRs, 2 waves per SIMD), so a 512-thread
+// faster.  The backward holds more per thread (232 VGPRs, 2 waves per SIMD), so a 512-thread
 // workgroup would leave one workgroup per CU; it keeps 256 threads.
 // A thread holds at most 32 elements per step group: four steps of 8 channels, or two steps
 // of 16 channels for one-byte storage (more would spill the backward's registers).  The
-// one-byte forward needs 132 VGPRs, which fit three waves per SIMD: 256-thread workgroups
+// one-byte forward needs 136 VGPRs, which fit three waves per SIMD: 256-thread workgroups
 // then run three to a CU, measured 1.45x faster at 64K context than one 512-thread
 // workgroup per CU.
 template <typename T, int DH>
@@ -128,7 +128,7 @@ struct BwdCfg {
     static constexpr int S0 = Geom<T, DH, 1, NT>::S;
     // four steps per thread (at least 64 steps per tile): deeper tiles halve the look-back
     // words against two steps per thread and measured ~3 % faster at 64K context, although
-    // the 231 VGPRs then allow two waves per SIMD rather than three
+    // the 232 VGPRs then allow two waves per SIMD rather than three
     static constexpr int LR = 32 / Storage<T>::VEC < 4 ? 32 / Storage<T>::VEC : 4;
     static constexpr int L = LR * S0 >= kCkptChunk ? LR : kCkptChunk / S0;
     using G = Geom<T, DH, L, NT>;
