@@ -377,6 +377,38 @@ def test_long64k_shapes_in_fp32_8gib_tensors():
     torch.cuda.empty_cache()
 
 
+def test_rows_wider_than_a_32_bit_tile_span():
+    """C = 8M channels (H = 131072 heads of 64) in fp16: one tile's rows span 2^32 bytes in the
+    forward and 2^31 in the backward, beyond the 32-bit lane offsets of the buffer-addressed
+    path, so every tile takes the 64-bit-addressed path.  T = 300 leaves ragged last tiles.
+    Sampled heads are compared with the oracle (heads are independent)."""
+    B, T, H, Dh = 1, 300, 131072, 64
+    dt, mode = torch.float16, "controlled"
+    say(f"wide rows C={H * Dh}")
+    shp = (B, T, H, Dh)
+    g = {k: synth.normal(shp, 960 + i, 1.0 if k == "a" else 0.0, 1.0, dt, DEV)
+         for i, k in enumerate(("a", "v", "q", "dy"))}
+    e0 = synth.random_state(B, H, Dh, 965, DEV)
+    dET = synth.random_state(B, H, Dh, 966, DEV)
+    y, eT, ck = binding.scan_fwd(g["a"], g["v"], g["q"], e0, mode=mode, return_ckpt=True)
+    da, dv, dq, de0 = binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], e0, dET, ckpt=ck,
+                                       mode=mode)
+    torch.cuda.synchronize()
+    check_abort_clear()
+    heads = [0, 1, 4097, H // 2, H - 1]
+    c = {k: t[:, :, heads].cpu() for k, t in g.items()}
+    ce0, cdET = e0[:, heads].cpu(), dET[:, heads].cpu()
+    ry, reT = oracle.scan_fwd(c["a"], c["v"], c["q"], ce0, mode=MODES[mode])
+    assert_close("y", y[:, :, heads].cpu(), ry, dt)
+    assert_close("eT", eT[:, heads].cpu(), reT, dt)
+    r = oracle.scan_bwd(c["a"], c["v"], c["q"], c["dy"], ce0, cdET, mode=MODES[mode])
+    for name, got, ref in zip(("d_logit", "d_value", "d_query"), (da, dv, dq), r):
+        assert_close(name, got[:, :, heads].cpu(), ref, dt)
+    assert_close("d_init", de0[:, heads].cpu(), r[3], dt)
+    del g, y, eT, ck, da, dv, dq, de0
+    torch.cuda.empty_cache()
+
+
 def test_workload_long64k_f8e4m3():
     wl = synth.WORKLOADS["long64k_f8e4m3"]
     say(f"workload {wl.name}")
