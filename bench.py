@@ -329,6 +329,18 @@ def bench_variants(args, torch, binding, synth):
     return out
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, train):
     """The oracle, as it stands, on the 64K workload's own inputs: whole batch rows (every row
     is an independent problem), one row per thread, fwd + bwd, in batches of `threads` rows
@@ -353,7 +365,7 @@ def cpu_baseline(args, train):
         del a, v, q, dy
     T = x["a"].shape[1]
     return {"value": rows * T / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": sec,
+            "seconds": sec, "host_cpus": os.cpu_count(), "cpu_model": host_cpu_model(),
             "sample": f"{rows} of the {B} batch rows x T={T} (H=8, Dh=64, fp64, controlled) "
                       f"fwd+bwd, one row per thread, {threads} threads"}
 
