@@ -229,8 +229,10 @@ def scan_fwd(a, v, q, init_state=None, mode="controlled", return_ckpt=False, fin
 
 
 def scan_bwd(a, v, q, dy, init_state=None, d_final_state=None, ckpt=None, mode="controlled",
-             workspace=None, deterministic=False):
-    """Backward of scan_fwd (esa_scan_bwd).  Returns (d_logit, d_value, d_query, d_init)."""
+             workspace=None, deterministic=False, d_logit=None, d_value=None, d_query=None,
+             d_init=None):
+    """Backward of scan_fwd (esa_scan_bwd).  Returns (d_logit, d_value, d_query, d_init);
+    any of the four may be passed in to be written in place."""
     lib = load_library()
     a = _seq("gate_logit", a)
     v = _seq("value", v, a)
@@ -243,10 +245,18 @@ def scan_bwd(a, v, q, dy, init_state=None, d_final_state=None, ckpt=None, mode="
         if ckpt.dtype != torch.float32 or ckpt.numel() * 4 < ckpt_bytes(B, T, H, Dh):
             raise ValueError("ckpt must be the fp32 checkpoint of scan_fwd(return_ckpt=True)")
         ckpt = ckpt.contiguous()
-    da = torch.empty_like(a)
-    dv = torch.empty_like(a)
-    dq = torch.empty_like(a)
-    d_init = torch.empty((B, H, Dh), dtype=torch.float32, device=a.device)
+    grads = []
+    for name, t in (("d_logit", d_logit), ("d_value", d_value), ("d_query", d_query)):
+        if t is None:
+            t = torch.empty_like(a)
+        else:
+            _out(name, t, a.shape, a.dtype, a.device)
+        grads.append(t)
+    da, dv, dq = grads
+    if d_init is None:
+        d_init = torch.empty((B, H, Dh), dtype=torch.float32, device=a.device)
+    else:
+        _out("d_init", d_init, (B, H, Dh), torch.float32, a.device)
     need = workspace_bytes(B, T, H, Dh, a.dtype)
     ws = workspace if workspace is not None else get_workspace(need, a.device)
     with _OnDevice(a.device.index):

@@ -233,6 +233,22 @@ def test_binding_rejects_mismatched_outputs():
         binding.state_step(a1, v1, q1, st.to(torch.float16))
     with pytest.raises(ValueError):
         binding.state_step(a1, v1, q1, st.cpu())
+    # backward outputs: wrong ones are rejected; right ones are written in place
+    dy = x["a"].flip(1).contiguous()
+    _, _, ck = binding.scan_fwd(x["a"], x["v"], x["q"], return_ckpt=True)
+    for kw in ({"d_logit": bad_y[0]}, {"d_value": bad_y[1]}, {"d_query": bad_y[2]},
+               {"d_init": torch.empty(B, H, Dh, device=DEV, dtype=torch.float16)}):
+        with pytest.raises(ValueError):
+            binding.scan_bwd(x["a"], x["v"], x["q"], dy, ckpt=ck, deterministic=True, **kw)
+    ref = binding.scan_bwd(x["a"], x["v"], x["q"], dy, ckpt=ck, deterministic=True)
+    outs = [torch.full_like(x["a"], float("nan")) for _ in range(3)]
+    outs.append(torch.full((B, H, Dh), float("nan"), device=DEV))
+    got = binding.scan_bwd(x["a"], x["v"], x["q"], dy, ckpt=ck, deterministic=True,
+                           d_logit=outs[0], d_value=outs[1], d_query=outs[2], d_init=outs[3])
+    torch.cuda.synchronize()
+    for g_, o_, r_ in zip(got, outs, ref):
+        assert g_ is o_
+        assert torch.equal(g_, r_)
 
 
 def test_saturated_gates_reach_special_cases():
