@@ -117,7 +117,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             float s, u;
-            gate(av[e], s, u);
+            gate<T>(av[e], s, u);
             s = ok ? s : 1.0f;
             u = ok ? u : 0.0f;
             S_[i][e] = s;

@@ -391,12 +391,22 @@ __device__ __forceinline__ void st16(void* base, int64_t elem_off, int esize, co
 // that it keeps full relative precision when s is close to 1.  exp(-a) is capped at 2^126 so
 // that 1 + exp(-a) stays finite (for a < -87 the true s is below 2^-126 and 2^-126 is used);
 // a NaN logit stays NaN.
+//
+// With fp32 storage (the tightest parity bar) s itself is taken as 1 - u when a > 0: u is
+// relatively exact, so 1 - u is s correctly rounded, whereas 1 / (1 + e) carries the rounding
+// of 1 + e and of the reciprocal (measured: off by one unit in the last place in half the
+// cases, with a bias).  A retentive chain (1 - s ~ 1e-4) sums that bias over its ~1 / (1 - s)
+// steps of memory: at a ~ N(6, 1) over 15000 steps the largest error (in the gate gradient)
+// drops from 8.8e-5 to 1.5e-5 and that of y from 1.4e-5 to 5.4e-6.  The extra instructions are skipped for 16- and 8-bit storage, whose bars are
+// orders of magnitude wider than this error.
+template <typename T>
 __device__ __forceinline__ void gate(float a, float& s, float& u) {
     float x = a * -1.4426950408889634f;  // -a * log2(e)
     x = x > 126.0f ? 126.0f : x;
     const float e = __builtin_amdgcn_exp2f(x);
     s = __builtin_amdgcn_rcpf(1.0f + e);
     u = e * s;
+    if constexpr (sizeof(T) == 4) s = a > 0.0f ? 1.0f - u : s;
 }
 
 // Sum over the HL consecutive, aligned threads that hold one head; every thread of the head

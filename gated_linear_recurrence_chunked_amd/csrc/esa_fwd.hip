@@ -90,7 +90,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             float s, u;
-            gate(av[e], s, u);
+            gate<T>(av[e], s, u);
             const float bt = MODE == kDirect ? vv[e] : u * vv[e];
             A[i][e] = ok ? s : 1.0f;
             Bt[i][e] = ok ? bt : 0.0f;

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
         float s, u;
-        gate(av[e], s, u);
+        gate<T>(av[e], s, u);
         st[e] = s * st[e] + (MODE == kDirect ? vv[e] : u * vv[e]);
         ss += st[e] * st[e];
     }

@@ -14,10 +14,15 @@ import torch
 
 # fp8 storage: the outputs are rounded once to the 8-bit format, whose relative rounding
 # error is at most 2^-4 (E4M3, 3 stored mantissa bits) or 2^-3 (E5M2, 2 bits) in the normal
-# range; below it the rounding is absolute (at most 2^-10 for E4M3, 2^-17 for E5M2) and the
-# metric scales it by rms(r).  The fp32 arithmetic adds ~1e-6 on top.
+# range; below it the rounding is absolute, at most half the subnormal step: 2^-10 for E4M3,
+# 2^-17 for E5M2.  The fp32 arithmetic adds ~1e-6 on top.
 TOL = {torch.float32: 1e-5, torch.float16: 5e-3, torch.bfloat16: 5e-3,
        torch.float8_e4m3fn: 2.0 ** -4 + 1e-4, torch.float8_e5m2: 2.0 ** -3 + 1e-4}
+# The scale floor that makes the fp8 bar cover that absolute half step: the smallest normal
+# number, 2^-6 (E4M3) and 2^-14 (E5M2), times the relative bar is the half step.  Without it
+# an output whose every value is subnormal (a gate gradient s (1 - s) dE E of a retentive
+# gate, say) fails on correct rounding alone.
+FLOOR = {torch.float8_e4m3fn: 2.0 ** -6, torch.float8_e5m2: 2.0 ** -14}
 
 
 def f64(x):
@@ -44,7 +49,7 @@ def err(x, r, floor: float = 0.0) -> float:
 
 
 def assert_close(name, x, r, dtype, floor: float = 0.0):
-    e = err(x, r, floor)
+    e = err(x, r, max(floor, FLOOR.get(dtype, 0.0)))
     tol = TOL[dtype]
     print(f"  {name}: err {e:.3e} (bar {tol:.0e})", flush=True)
     assert e <= tol, f"{name}: err {e:.3e} > tol {tol:.0e}"

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import TOL, err
+from helpers import FLOOR, TOL, err
 
 FORMATS = {
     # name: (torch dtype, exponent bits, mantissa bits, bias, has infinities)
@@ -71,3 +71,20 @@ def test_bar_covers_one_rounding_and_not_two_steps(dt):
     up = up.clamp(0, 255).to(torch.uint8).view(dt)
     fin = torch.isfinite(up.double())
     assert err(up.double()[fin], x[fin]) > TOL[dt]
+
+
+@pytest.mark.parametrize("dt", [torch.float8_e4m3fn, torch.float8_e5m2])
+def test_bar_covers_subnormal_rounding_and_not_a_subnormal_step(dt):
+    """Below the smallest normal number the formats round to a fixed absolute step; with the
+    scale floor of the fp8 bar (the smallest normal), one correct rounding of values that are
+    all subnormal passes and an error of one subnormal step fails."""
+    g = torch.Generator().manual_seed(6)
+    tiny = FLOOR[dt] / 4  # draws mostly below the smallest normal
+    x = torch.randn(200000, generator=g, dtype=torch.float64) * tiny
+    r = x.to(dt)
+    assert err(r, x, FLOOR[dt]) <= TOL[dt]
+    assert err(r, x) > TOL[dt]  # the unfloored metric rejects correct rounding here
+    up = (r.view(torch.uint8).to(torch.int32) + torch.where(r.double() >= 0, 1, -1))
+    up = up.clamp(0, 255).to(torch.uint8).view(dt)
+    fin = torch.isfinite(up.double())
+    assert err(up.double()[fin], x[fin], FLOOR[dt]) > TOL[dt]
