@@ -327,6 +327,38 @@ def test_resume_equals_unsplit():
     assert err(e2, eT) <= 1e-5
 
 
+@pytest.mark.parametrize("mode", ["direct", "controlled"])
+def test_causality(mode):
+    """The readout at t depends on no input after t, and the gradients at t on no upstream
+    gradient before t (the pages' "causal behavior" test of page "entangled-state-attention
+    0.1.0", on the GPU path).  Every input from a mid-tile step t0 on is redrawn: y before t0
+    keeps its bits (deterministic look-back, so a changed carry would show).  Then every dy
+    before t0 is redrawn: the gradients from t0 on keep their bits."""
+    say(f"causality {mode}")
+    B, T, H, Dh, t0 = 2, 3000, 2, 64, 1234
+    x = {k: t.to(DEV) for k, t in inputs_cpu(B, T, H, Dh, torch.float16, seed=81, dy=True).items()}
+    z = {k: t.to(DEV) for k, t in inputs_cpu(B, T, H, Dh, torch.float16, seed=82, dy=True).items()}
+    x2 = {k: x[k].clone() for k in x}
+    for k in ("a", "v", "q"):
+        x2[k][:, t0:] = z[k][:, t0:]
+    y1, e1, ck1 = binding.scan_fwd(x["a"], x["v"], x["q"], mode=mode, return_ckpt=True,
+                                   deterministic=True)
+    y2, e2, _ = binding.scan_fwd(x2["a"], x2["v"], x2["q"], mode=mode, return_ckpt=True,
+                                 deterministic=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1[:, :t0], y2[:, :t0])
+    assert not torch.equal(y1[:, t0:], y2[:, t0:])
+    dy2 = x["dy"].clone()
+    dy2[:, :t0] = z["dy"][:, :t0]
+    g1 = binding.scan_bwd(x["a"], x["v"], x["q"], x["dy"], ckpt=ck1, mode=mode,
+                          deterministic=True)
+    g2 = binding.scan_bwd(x["a"], x["v"], x["q"], dy2, ckpt=ck1, mode=mode, deterministic=True)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(g1[:3], g2[:3]):
+        assert torch.equal(a_[:, t0:], b_[:, t0:])
+        assert not torch.equal(a_[:, :t0], b_[:, :t0])
+
+
 # ---------------------------------------------------------------------------------------
 # The workloads at full size, compared on sampled batch rows.
 # ---------------------------------------------------------------------------------------
