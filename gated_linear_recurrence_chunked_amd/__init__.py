@@ -7,13 +7,18 @@ does, and fails loudly when the library is missing.
 """
 from __future__ import annotations
 
-__all__ = ["scan_fwd", "scan_bwd", "state_step", "StepPlan", "segment_fwd", "segment_bwd",
-           "segment_compose", "workspace_bytes", "ckpt_bytes", "EsaError", "library_path",
-           "load_library"]
+_BINDING = ["scan_fwd", "scan_bwd", "state_step", "StepPlan", "segment_fwd", "segment_bwd",
+            "segment_compose", "workspace_bytes", "ckpt_bytes", "EsaError", "library_path",
+            "load_library"]
+_AUTOGRAD = ["esa_scan", "ESALayer"]
+__all__ = _BINDING + _AUTOGRAD
 
 
 def __getattr__(name):
-    if name in __all__:
+    if name in _BINDING:
         from . import binding
         return getattr(binding, name)
+    if name in _AUTOGRAD:
+        from . import autograd
+        return getattr(autograd, name)
     raise AttributeError(name)

@@ -195,3 +195,13 @@ def test_segment_validation(lib):
     assert compose(total=3) == INVALID  # total overlaps carry
     assert compose(x=ctypes.c_void_p(0x100000000 + 0x20000000 + 2)) == INVALID  # misaligned
     assert compose(nseg=1 << 40, lanes=1 << 40) == INVALID  # size overflows
+
+
+def test_public_names_resolve():
+    """Every name the package exports resolves (the pages' test list includes the public
+    imports); none needs a GPU to be looked up."""
+    import gated_linear_recurrence_chunked_amd as pkg
+
+    for name in pkg.__all__:
+        assert getattr(pkg, name) is not None, name
+    from gated_linear_recurrence_chunked_amd import ESALayer, esa_scan, scan_fwd, state_step  # noqa: F401
