@@ -212,15 +212,17 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         float carry = 0.0f;
         if (FULL || gl < p.nLanes) {
             uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
+            bool pub = true;
             if (tile == p.nTiles - 1) {
                 carry = p.dET ? p.dET[gl] : 0.0f;
+                pub = !withheld(p.hdr);
             } else {
                 float pin;  // unused: the backward carries no gate product
                 carry = chain_carry(p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc,
                                     p.hdr, tp, te, &pin, p.det != 0);
             }
             const float lam_out = te + tp * carry;
-            publish(X, tagInc, lam_out);
+            if (pub) publish(X, tagInc, lam_out);
             if (tile == 0 && p.de0) p.de0[gl] = lam_out;
         }
         sCarry[ch] = carry;

@@ -139,10 +139,17 @@ struct BwdCfg {
 // Workspace layout: [header 256 B][flag X words][flag Y words][internal checkpoint].
 struct WsHeader {
     uint32_t epoch;  // device epoch of launches recorded into graphs (bit 29 set once used)
-    uint32_t reserved[2];
+    // Test controls, zero in normal use: a nonzero spin_limit replaces kSpinLimit, and a
+    // nonzero withhold makes the first tile of every chain skip its publications, so that
+    // every wait on it times out (a failure forced from the host; each wait still ends).
+    uint32_t spin_limit;
+    uint32_t withhold;
     uint32_t abort;  // sticky: set when a look-back wait timed out (results are then NaN)
     uint32_t pad[60];
 };
+constexpr int kHdrSpinLimit = 1;  // word indices of the header fields read by the kernels
+constexpr int kHdrWithhold = 2;
+constexpr int kHdrAbort = 3;
 constexpr uint32_t kHostEpochMask = 0x1fffffffu;  // host epochs: bit 29 clear
 constexpr uint32_t kDeviceEpochBit = 0x20000000u;  // device epochs: bit 29 set
 static_assert(sizeof(WsHeader) == 256, "header must be 256 bytes");
@@ -573,15 +580,25 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 // abort word is set, or this wait has polled kSpinLimit times; then it sets the abort word).
 __device__ __forceinline__ bool wait_turn(uint32_t polls, uint32_t* hdr) {
     if ((polls & 255u) == 0u) {
-        const bool abort =
-            __hip_atomic_load(&hdr[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-        if (abort || polls >= kSpinLimit) {
-            if (!abort) __hip_atomic_store(&hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool abort = __hip_atomic_load(&hdr[kHdrAbort], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) != 0u;
+        const uint32_t lim = __hip_atomic_load(&hdr[kHdrSpinLimit], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        if (abort || polls >= (lim ? lim : kSpinLimit)) {
+            if (!abort)
+                __hip_atomic_store(&hdr[kHdrAbort], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return false;
         }
     }
     __builtin_amdgcn_s_sleep(1);
     return true;
+}
+
+// True when the host asked the chain's first tile to withhold its publications (a test
+// control of the workspace header; read only by that tile).
+__device__ __forceinline__ bool withheld(const uint32_t* hdr) {
+    return __hip_atomic_load(const_cast<uint32_t*>(&hdr[kHdrWithhold]), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) != 0u;
 }
 
 template <bool PROD = false>

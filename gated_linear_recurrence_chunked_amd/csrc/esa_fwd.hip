@@ -117,17 +117,19 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
             uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
             uint64_t* Y = p.flagY + (int64_t)tile * p.nLanes + gl;
             float pin = 1.0f;  // PROD: product of the gates of every earlier tile
+            bool pub = true;
             if (tile == 0) {
                 carry = p.e0 ? p.e0[gl] : 0.0f;
+                pub = !withheld(p.hdr);
             } else {
                 carry = chain_carry<PROD>(p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg,
                                           tagInc, p.hdr, tp, te, &pin, p.det != 0);
             }
             if constexpr (PROD) {
-                publish(Y, tagInc, tp * pin);
+                if (pub) publish(Y, tagInc, tp * pin);
                 if (tile == p.nTiles - 1) p.prod[gl] = tp * pin;
             }
-            publish(X, tagInc, te + tp * carry);
+            if (pub) publish(X, tagInc, te + tp * carry);
         }
         sCarry[ch] = carry;
     }

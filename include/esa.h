@@ -115,8 +115,13 @@ size_t esa_scan_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t Dh);
 
 /* Zero-fills `bytes` of workspace on `stream` (a fill kernel, safe inside graph capture).
  * Word 3 of the workspace (bytes 12..15) is a sticky abort flag: it becomes non-zero if a
- * scan's cross-tile wait ever timed out (about a second), in which case that call's results
- * are NaN.  This never happens in a correct run; re-initialising the workspace clears it. */
+ * scan's cross-tile wait ever timed out (about a second), in which case the outputs that
+ * depend on the missing value are NaN.  This never happens in a correct run;
+ * re-initialising the workspace clears it.  Words 1 and 2 (bytes 4..11) are test controls
+ * that stay zero in normal use: a non-zero word 1 replaces the wait's poll limit, and a
+ * non-zero word 2 makes the first tile of every chain (first in the scan's direction)
+ * withhold its published values, so every wait on them times out: a failure forced from
+ * the host in which every wait still ends. */
 int esa_workspace_init(void *workspace, size_t bytes, void *stream);
 
 /* Forward scan with fused gate and readout: prefill and training forward (page "Entangled

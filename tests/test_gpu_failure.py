@@ -1,0 +1,99 @@
+"""A look-back failure forced from the host, through the workspace header's test controls:
+the first tile of every chain withholds its published values (word 2) and the wait's poll
+limit is made small (word 1), so every wait on a withheld value ends by timing out.  The
+call still returns; the sticky abort word (word 3) is set; the outputs of the first tile
+are exact and every output that depends on the withheld values is NaN; re-initialising the
+workspace with esa_workspace_init restores normal runs."""
+import ctypes
+import sys
+
+import pytest
+import torch
+
+from gated_linear_recurrence_chunked_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def header(ws):
+    return ws[:16].view(torch.int32)
+
+
+def first_nan_step(t):
+    """Index along T of the first step holding a NaN ([B, T, H, Dh] tensor), or T."""
+    bad = torch.isnan(t.float()).flatten(2).any(-1).any(0)
+    idx = torch.nonzero(bad)
+    return int(idx[0]) if len(idx) else t.shape[1]
+
+
+def last_nan_step(t):
+    bad = torch.isnan(t.float()).flatten(2).any(-1).any(0)
+    idx = torch.nonzero(bad)
+    return int(idx[-1]) if len(idx) else -1
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_withheld_first_tile_times_out_to_nan(det):
+    B, T, H, Dh = 2, 1000, 2, 64
+    dt, mode = torch.float16, "controlled"
+    say(f"forced look-back failure det={det}")
+    shp = (B, T, H, Dh)
+    x = {k: synth.normal(shp, 970 + i, 1.0 if k == "a" else 0.0, 1.0, dt).to(DEV)
+         for i, k in enumerate(("a", "v", "q", "dy"))}
+    y0, eT0, ck0 = binding.scan_fwd(x["a"], x["v"], x["q"], mode=mode, return_ckpt=True,
+                                    deterministic=True)
+    g0 = binding.scan_bwd(x["a"], x["v"], x["q"], x["dy"], ckpt=ck0, mode=mode,
+                          deterministic=True)
+    ws = torch.zeros(binding.workspace_bytes(B, T, H, Dh, dt), dtype=torch.uint8, device=DEV)
+
+    # forward: the chain's first tile withholds; every later tile's carry is NaN
+    h = header(ws)
+    h[1] = 4096
+    h[2] = 1
+    y, eT, ck = binding.scan_fwd(x["a"], x["v"], x["q"], mode=mode, return_ckpt=True,
+                                 workspace=ws, deterministic=det)
+    torch.cuda.synchronize()
+    assert int(h[3]) != 0, "the abort word is set"
+    k = first_nan_step(y)
+    say(f"  forward: exact through step {k - 1}, NaN from step {k}")
+    assert 0 < k < T and k % 64 == 0
+    assert torch.equal(y[:, :k], y0[:, :k])
+    assert torch.isnan(y[:, k:].float()).all()
+    assert torch.isnan(eT).all()
+
+    # backward (from the good checkpoint): the chain starts at the last tile
+    h.zero_()
+    h[1] = 4096
+    h[2] = 1
+    da, dv, dq, de0 = binding.scan_bwd(x["a"], x["v"], x["q"], x["dy"], ckpt=ck0, mode=mode,
+                                       workspace=ws, deterministic=det)
+    torch.cuda.synchronize()
+    assert int(h[3]) != 0
+    j = last_nan_step(da)
+    say(f"  backward: NaN through step {j}, exact from step {j + 1}")
+    assert 0 <= j < T - 1 and (j + 1) % 64 == 0
+    for got, ref in ((da, g0[0]), (dv, g0[1])):
+        assert torch.equal(got[:, j + 1:], ref[:, j + 1:])
+        assert torch.isnan(got[:, :j + 1].float()).all()
+    assert torch.equal(dq, g0[2])  # the query gradient needs no carry
+    assert torch.isnan(de0).all()
+
+    # re-initialised through the library, the workspace serves normal runs again
+    lib = binding.load_library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.esa_workspace_init(ctypes.c_void_p(ws.data_ptr()), ws.numel(), stream) == 0
+    y1, eT1, ck1 = binding.scan_fwd(x["a"], x["v"], x["q"], mode=mode, return_ckpt=True,
+                                    workspace=ws, deterministic=True)
+    g1 = binding.scan_bwd(x["a"], x["v"], x["q"], x["dy"], ckpt=ck1, mode=mode, workspace=ws,
+                          deterministic=True)
+    torch.cuda.synchronize()
+    assert int(h[3]) == 0
+    assert torch.equal(y1, y0) and torch.equal(eT1, eT0)
+    for a_, b_ in zip(g1, g0):
+        assert torch.equal(a_, b_)
