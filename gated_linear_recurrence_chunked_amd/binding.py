@@ -37,6 +37,7 @@ DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4
           torch.float8_e5m2: 4}
 MODES = {"direct": 0, "controlled": 1}
 DETERMINISTIC = 0x100  # ESA_DETERMINISTIC: OR-ed into the mode, bitwise reproducible scans
+TEST_FORCE_TIMEOUT = 0x200  # ESA_TEST_FORCE_TIMEOUT: a look-back timeout forced for tests
 
 # every function include/esa.h declares: name -> (restype, argtypes)
 _P = ctypes.c_void_p

@@ -19,6 +19,7 @@ struct Problem {
     int64_t B, T, H, Dh, C, nLanes, nElem;
     int dtype, mode;  // mode: the recurrence form (ESA_DIRECT / ESA_CONTROLLED)
     uint32_t det;     // ESA_DETERMINISTIC was set
+    uint32_t forceTimeout;  // ESA_TEST_FORCE_TIMEOUT was set
     int64_t esize;
 };
 
@@ -69,7 +70,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int check_sizes(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode, Problem* pr) {
-    const int form = mode & ~ESA_DETERMINISTIC;
+    const int form = mode & ~(ESA_DETERMINISTIC | ESA_TEST_FORCE_TIMEOUT);
     if (dtype < ESA_F32 || dtype > ESA_F8E5M2 || form < ESA_DIRECT || form > ESA_CONTROLLED)
         return ESA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || Dh < 1 || T < 0) return ESA_ERR_INVALID_ARG;
@@ -81,12 +82,21 @@ int check_sizes(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode
     pr->dtype = dtype;
     pr->mode = form;
     pr->det = (mode & ESA_DETERMINISTIC) ? 1u : 0u;
+    pr->forceTimeout = (mode & ESA_TEST_FORCE_TIMEOUT) ? 1u : 0u;
     pr->esize = storage_bytes(dtype);
     int64_t bytes;
     if (!mul64(H, Dh, &pr->C) || !mul64(B, pr->C, &pr->nLanes) || !mul64(pr->nLanes, T, &pr->nElem) ||
         !mul64(pr->nElem, 4, &bytes) || !mul64(pr->nLanes, 16, &bytes))
         return ESA_ERR_INVALID_ARG;
     return ESA_OK;
+}
+
+// ESA_TEST_FORCE_TIMEOUT is accepted by the readout forward and the gradient backward, for
+// fp16 storage and Dh = 64 (the problems with a test instance of the kernels).
+int check_test_flag(const Problem& pr, bool call_allows_it) {
+    if (!pr.forceTimeout) return ESA_OK;
+    if (!call_allows_it) return ESA_ERR_INVALID_ARG;
+    return pr.dtype == ESA_F16 && pr.Dh == 64 ? ESA_OK : ESA_ERR_UNSUPPORTED;
 }
 
 struct Layout {
@@ -223,6 +233,8 @@ int scan_bwd_impl(bool grads, int64_t B, int64_t T, int64_t H, int64_t Dh, int d
     Problem pr;
     int rc = check_sizes(B, T, H, Dh, dtype, mode, &pr);
     if (rc != ESA_OK) return rc;
+    rc = check_test_flag(pr, grads);
+    if (rc != ESA_OK) return rc;
     if (T > 0 && (!gate_logit || !value || !query || !dy)) return ESA_ERR_INVALID_ARG;
     if (grads ? (T > 0 && (!d_gate_logit || !d_value || !d_query))
               : (d_gate_logit || d_value || d_query || !d_init_state))
@@ -271,6 +283,7 @@ int scan_bwd_impl(bool grads, int64_t B, int64_t T, int64_t H, int64_t Dh, int d
         f.nCB = L.nCB;
         f.nTiles = L.nTilesF;
         f.det = pr.det;
+        f.withhold = 0;  // the checkpoint pass never takes the test instance
         rc = set_epoch(s, hdr, &f.epoch, &f.epochWord);
         if (rc != ESA_OK) return rc;
         rc = hip_status(ESA_DISPATCH(fwd, dtype, pr.mode, Dh, f, s));
@@ -299,6 +312,7 @@ int scan_bwd_impl(bool grads, int64_t B, int64_t T, int64_t H, int64_t Dh, int d
     p.nCB = L.nCB;
     p.nTiles = L.nTilesB;
     p.det = pr.det;
+    p.withhold = pr.forceTimeout;
     rc = set_epoch(s, hdr, &p.epoch, &p.epochWord);
     if (rc != ESA_OK) return rc;
     return hip_status(ESA_DISPATCH(bwd, dtype, pr.mode, Dh, p, s));
@@ -350,6 +364,8 @@ int esa_scan_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mod
     Problem pr;
     int rc = check_sizes(B, T, H, Dh, dtype, mode, &pr);
     if (rc != ESA_OK) return rc;
+    rc = check_test_flag(pr, true);
+    if (rc != ESA_OK) return rc;
     if (T > 0 && (!gate_logit || !value || !query || !y)) return ESA_ERR_INVALID_ARG;
     const void* ptrs[] = {gate_logit, value, query, init_state, y, final_state, ckpt, workspace};
     for (const void* q : ptrs)
@@ -391,6 +407,7 @@ int esa_scan_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mod
     p.nCB = L.nCB;
     p.nTiles = L.nTilesF;
     p.det = pr.det;
+    p.withhold = pr.forceTimeout;
     rc = set_epoch(s, p.hdr, &p.epoch, &p.epochWord);
     if (rc != ESA_OK) return rc;
     return hip_status(ESA_DISPATCH(fwd, dtype, pr.mode, Dh, p, s));
@@ -410,6 +427,8 @@ int esa_state_step(int64_t B, int64_t H, int64_t Dh, int dtype, int mode, const 
                    const void* value, const void* query, float* state, void* y, void* stream) {
     Problem pr;
     int rc = check_sizes(B, 1, H, Dh, dtype, mode, &pr);
+    if (rc != ESA_OK) return rc;
+    rc = check_test_flag(pr, false);
     if (rc != ESA_OK) return rc;
     if (!gate_logit || !value || !query || !state || !y) return ESA_ERR_INVALID_ARG;
     const void* ptrs[] = {gate_logit, value, query, state, y};
@@ -435,6 +454,8 @@ int esa_scan_segment_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype,
                          void* stream) {
     Problem pr;
     int rc = check_sizes(B, T, H, Dh, dtype, mode, &pr);
+    if (rc != ESA_OK) return rc;
+    rc = check_test_flag(pr, false);
     if (rc != ESA_OK) return rc;
     if (!seg_state || !seg_gate_prod) return ESA_ERR_INVALID_ARG;
     if (T > 0 && (!gate_logit || !value)) return ESA_ERR_INVALID_ARG;
@@ -473,6 +494,7 @@ int esa_scan_segment_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype,
     f.nCB = L.nCB;
     f.nTiles = L.nTilesF;
     f.det = pr.det;
+    f.withhold = 0;
     rc = set_epoch(s, f.hdr, &f.epoch, &f.epochWord);
     if (rc != ESA_OK) return rc;
     return hip_status(ESA_DISPATCH(fwd, dtype, pr.mode, Dh, f, s));

@@ -23,7 +23,7 @@
 
 namespace esa {
 
-template <typename T, int MODE, int DH, int L, int NT, bool GRADS, bool FULL>
+template <typename T, int MODE, int DH, int L, int NT, bool GRADS, bool FULL, bool TEST>
 __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint32_t cb, float* sP,
                                          float* sE, float* sWP, float* sWE, float* sCarry) {
     using G = Geom<T, DH, L, NT>;
@@ -212,17 +212,17 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         float carry = 0.0f;
         if (FULL || gl < p.nLanes) {
             uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
-            bool pub = true;
             if (tile == p.nTiles - 1) {
                 carry = p.dET ? p.dET[gl] : 0.0f;
-                pub = !withheld(p.hdr);
             } else {
                 float pin;  // unused: the backward carries no gate product
-                carry = chain_carry(p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc,
-                                    p.hdr, tp, te, &pin, p.det != 0);
+                carry = chain_carry<false, TEST ? kTestSpinLimit : kSpinLimit>(
+                    p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc, p.hdr, tp, te, &pin,
+                    p.det != 0);
             }
             const float lam_out = te + tp * carry;
-            if (pub) publish(X, tagInc, lam_out);
+            if (!TEST || tile != p.nTiles - 1)  // the test instance withholds the last tile
+                publish(X, tagInc, lam_out);
             if (tile == 0 && p.de0) p.de0[gl] = lam_out;
         }
         sCarry[ch] = carry;
@@ -257,7 +257,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     }
 }
 
-template <typename T, int MODE, int DH, int L, int NT, bool GRADS>
+template <typename T, int MODE, int DH, int L, int NT, bool GRADS, bool TEST = false>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     using G = Geom<T, DH, L, NT>;
     constexpr int CB = G::CB, TT = G::TT, NW = G::NW;
@@ -275,16 +275,23 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     const bool full = (int64_t)(tile + 1) * TT <= p.T && (int64_t)(cb + 1) * CB <= p.nLanes &&
                       p.C % CB == 0 && (int64_t)TT * p.C * (int64_t)sizeof(T) < (int64_t(1) << 31);
     if (full)
-        bwd_tile<T, MODE, DH, L, NT, GRADS, true>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
+        bwd_tile<T, MODE, DH, L, NT, GRADS, true, TEST>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
     else
-        bwd_tile<T, MODE, DH, L, NT, GRADS, false>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
+        bwd_tile<T, MODE, DH, L, NT, GRADS, false, TEST>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
 }
 
 template <typename T, int MODE, int DH>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
     using C = BwdCfg<T, DH>;
     const dim3 grid(p.nCB * p.nTiles), block(C::NT);
-    if (p.da)
+    if (p.da && p.withhold) {
+        // the forced-timeout test instance: fp16 storage and Dh = 64 only (as the forward)
+        if constexpr (std::is_same<T, _Float16>::value && DH == 64)
+            hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT, true, true>), grid, block, 0, s,
+                               p);
+        else
+            return hipErrorNotSupported;
+    } else if (p.da)
         hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT, true>), grid, block, 0, s, p);
     else
         hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT, false>), grid, block, 0, s, p);

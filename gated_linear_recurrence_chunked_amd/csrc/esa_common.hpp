@@ -43,6 +43,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace esa {
 
 constexpr int kWave = 64;
@@ -139,17 +141,10 @@ struct BwdCfg {
 // Workspace layout: [header 256 B][flag X words][flag Y words][internal checkpoint].
 struct WsHeader {
     uint32_t epoch;  // device epoch of launches recorded into graphs (bit 29 set once used)
-    // Test controls, zero in normal use: a nonzero spin_limit replaces kSpinLimit, and a
-    // nonzero withhold makes the first tile of every chain skip its publications, so that
-    // every wait on it times out (a failure forced from the host; each wait still ends).
-    uint32_t spin_limit;
-    uint32_t withhold;
+    uint32_t reserved[2];
     uint32_t abort;  // sticky: set when a look-back wait timed out (results are then NaN)
     uint32_t pad[60];
 };
-constexpr int kHdrSpinLimit = 1;  // word indices of the header fields read by the kernels
-constexpr int kHdrWithhold = 2;
-constexpr int kHdrAbort = 3;
 constexpr uint32_t kHostEpochMask = 0x1fffffffu;  // host epochs: bit 29 clear
 constexpr uint32_t kDeviceEpochBit = 0x20000000u;  // device epochs: bit 29 set
 static_assert(sizeof(WsHeader) == 256, "header must be 256 bytes");
@@ -178,6 +173,7 @@ struct FwdParams {
     uint32_t epoch;  // tags of this call's look-back words (host epoch)
     const uint32_t* epochWord;  // non-NULL: read the epoch here instead (graph-recorded launch)
     uint32_t det;    // non-zero: every tile waits for its neighbour's inclusive value
+    uint32_t withhold;  // non-zero: launch the forced-timeout test instance (see launch_fwd)
 };
 
 struct BwdParams {
@@ -204,6 +200,7 @@ struct BwdParams {
     uint32_t epoch;
     const uint32_t* epochWord;
     uint32_t det;
+    uint32_t withhold;
 };
 
 struct StepParams {
@@ -566,7 +563,8 @@ __device__ __forceinline__ float word_val(uint64_t w) {
 // tiles, forward scan) or +1 (toward later tiles, reverse scan).  Returns the carry entering
 // tile `tile`: the composition of the published pairs, ended by an inclusive value.
 //
-// The wait is bounded: after kSpinLimit polls without progress the workgroup raises the
+// The wait is bounded: after LIMIT polls without progress (kSpinLimit; kTestSpinLimit in the
+// forced-timeout test instances) the workgroup raises the
 // sticky abort word of the workspace header and returns NaN, and every other waiting
 // workgroup that sees the abort word returns NaN too, so a broken chain drains instead of
 // hanging.  A correct run never comes near the limit (about a second of polling).
@@ -575,18 +573,20 @@ __device__ __forceinline__ float word_val(uint64_t w) {
 // of every gate from the chain's start through that tile; *pinc then receives the product
 // through the tile before `tile` (NaN when the wait gave up).
 constexpr uint32_t kSpinLimit = 1u << 20;
+// The forced-timeout test instances (a separate kernel instantiation, so the normal kernels
+// carry no trace of it): the chain's first tile withholds its publications and every wait
+// gives up after kTestSpinLimit polls.
+constexpr uint32_t kTestSpinLimit = 4096;
 
 // One unproductive poll of a bounded wait: false once the wait must give up (the workspace's
-// abort word is set, or this wait has polled kSpinLimit times; then it sets the abort word).
+// abort word is set, or this wait has polled LIMIT times; then it sets the abort word).
+template <uint32_t LIMIT = kSpinLimit>
 __device__ __forceinline__ bool wait_turn(uint32_t polls, uint32_t* hdr) {
     if ((polls & 255u) == 0u) {
-        const bool abort = __hip_atomic_load(&hdr[kHdrAbort], __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT) != 0u;
-        const uint32_t lim = __hip_atomic_load(&hdr[kHdrSpinLimit], __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        if (abort || polls >= (lim ? lim : kSpinLimit)) {
-            if (!abort)
-                __hip_atomic_store(&hdr[kHdrAbort], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool abort =
+            __hip_atomic_load(&hdr[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+        if (abort || polls >= LIMIT) {
+            if (!abort) __hip_atomic_store(&hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return false;
         }
     }
@@ -594,14 +594,7 @@ __device__ __forceinline__ bool wait_turn(uint32_t polls, uint32_t* hdr) {
     return true;
 }
 
-// True when the host asked the chain's first tile to withhold its publications (a test
-// control of the workspace header; read only by that tile).
-__device__ __forceinline__ bool withheld(const uint32_t* hdr) {
-    return __hip_atomic_load(const_cast<uint32_t*>(&hdr[kHdrWithhold]), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT) != 0u;
-}
-
-template <bool PROD = false>
+template <bool PROD = false, uint32_t LIMIT = kSpinLimit>
 __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t* flagY,
                                            int64_t nLanes, int64_t lane, int64_t tile, int step,
                                            uint32_t tagAgg, uint32_t tagInc, uint32_t* hdr,
@@ -631,7 +624,7 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
                 continue;
             }
         }
-        if (!wait_turn(++polls, hdr)) {
+        if (!wait_turn<LIMIT>(++polls, hdr)) {
             if constexpr (PROD) *pinc = __builtin_nanf("");
             return __builtin_nanf("");
         }
@@ -651,7 +644,7 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
 // the same fp32 expression on every run (bitwise reproducible results), at the price of
 // resolving a chain's tiles one after another (free when a chain has about one tile
 // resident at a time, as at 64K context; ~10x slower for a single long chain).
-template <bool PROD = false>
+template <bool PROD = false, uint32_t LIMIT = kSpinLimit>
 __device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, int64_t nLanes,
                                              int64_t lane, int64_t tile, int step, uint32_t tagAgg,
                                              uint32_t tagInc, uint32_t* hdr, float tp, float te,
@@ -669,7 +662,7 @@ __device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, i
                     return word_val(x);
                 }
             }
-            if (!wait_turn(++polls, hdr)) {
+            if (!wait_turn<LIMIT>(++polls, hdr)) {
                 if constexpr (PROD) *pin = __builtin_nanf("");
                 return __builtin_nanf("");
             }
@@ -686,7 +679,8 @@ __device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, i
     }
     publish(flagX + tile * nLanes + lane, tagAgg, te);
     publish(flagY + tile * nLanes + lane, tagAgg, tp);
-    return look_back<PROD>(flagX, flagY, nLanes, lane, tile, step, tagAgg, tagInc, hdr, pin);
+    return look_back<PROD, LIMIT>(flagX, flagY, nLanes, lane, tile, step, tagAgg, tagInc, hdr,
+                                  pin);
 }
 
 // Workgroup -> (tile row, channel block).  Workgroup i runs on XCD i mod 8.  When the channel

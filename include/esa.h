@@ -57,8 +57,9 @@ extern "C" {
 #endif
 
 /* 1: fp32 / fp16 / bf16 storage.  2: adds the fp8 storage dtypes ESA_F8E4M3, ESA_F8E5M2,
- * the sequence-segment calls and the ESA_DETERMINISTIC mode flag. */
-#define ESA_ABI_VERSION 2
+ * the sequence-segment calls and the ESA_DETERMINISTIC mode flag.  3: adds the
+ * ESA_TEST_FORCE_TIMEOUT mode flag. */
+#define ESA_ABI_VERSION 3
 
 /* Checkpoint granularity: the forward can store the fp32 state at every 64th step. */
 #define ESA_CKPT_CHUNK 64
@@ -96,6 +97,16 @@ typedef enum { ESA_DIRECT = 0, ESA_CONTROLLED = 1 } esa_mode;
  * up to ~10x for a single long chain (B*H*Dh = 64).  esa_state_step accepts and ignores it. */
 #define ESA_DETERMINISTIC 0x100
 
+/* Test control OR-ed into the mode argument of esa_scan_fwd and esa_scan_bwd, never set in
+ * normal use: a separate instance of the kernels runs in which the first tile of every chain
+ * (first in the scan's direction) withholds its published values and the cross-tile wait
+ * gives up after a few thousand polls, so every wait on a withheld value times out.  The
+ * call returns normally: the workspace's abort word (see esa_workspace_init) is set, and
+ * every output that depends on a withheld value is NaN.  It exercises the failure path of
+ * the bounded wait from the host.  Only fp16 storage with Dh = 64 has that instance
+ * (ESA_ERR_UNSUPPORTED otherwise); the other calls reject the flag (ESA_ERR_INVALID_ARG). */
+#define ESA_TEST_FORCE_TIMEOUT 0x200
+
 /* ABI version of the loaded library (ESA_ABI_VERSION at build time). */
 int esa_abi_version(void);
 
@@ -116,12 +127,8 @@ size_t esa_scan_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t Dh);
 /* Zero-fills `bytes` of workspace on `stream` (a fill kernel, safe inside graph capture).
  * Word 3 of the workspace (bytes 12..15) is a sticky abort flag: it becomes non-zero if a
  * scan's cross-tile wait ever timed out (about a second), in which case the outputs that
- * depend on the missing value are NaN.  This never happens in a correct run;
- * re-initialising the workspace clears it.  Words 1 and 2 (bytes 4..11) are test controls
- * that stay zero in normal use: a non-zero word 1 replaces the wait's poll limit, and a
- * non-zero word 2 makes the first tile of every chain (first in the scan's direction)
- * withhold its published values, so every wait on them times out: a failure forced from
- * the host in which every wait still ends. */
+ * depend on the missing value are NaN.  This never happens in a correct run (it can be
+ * forced with ESA_TEST_FORCE_TIMEOUT); re-initialising the workspace clears it. */
 int esa_workspace_init(void *workspace, size_t bytes, void *stream);
 
 /* Forward scan with fused gate and readout: prefill and training forward (page "Entangled

@@ -47,7 +47,7 @@ def header_abi_version() -> int:
 
 
 def test_version_and_status_strings(lib):
-    assert lib.esa_abi_version() == header_abi_version() == 2
+    assert lib.esa_abi_version() == header_abi_version() == 3
     for s in range(5):
         assert lib.esa_status_string(s).decode().startswith(
             ["ESA_OK", "ESA_ERR_INVALID_ARG", "ESA_ERR_UNSUPPORTED", "ESA_ERR_WORKSPACE",
@@ -101,7 +101,9 @@ def test_fwd_validation(lib):
     assert fwd(lib, T=-1) == INVALID
     assert fwd(lib, dt=5) == INVALID
     assert fwd(lib, mode=0x102) == INVALID  # deterministic flag with a bad form
-    assert fwd(lib, mode=0x200) == INVALID  # unknown flag
+    assert fwd(lib, mode=0x400) == INVALID  # unknown flag
+    assert fwd(lib, mode=0x202) == INVALID  # test flag with a bad form
+    assert fwd(lib, Dh=64, mode=0x301, y=1) == INVALID  # both flags: the rest still validates
     assert fwd(lib, mode=0x101, y=1) == INVALID  # a valid flagged mode still validates the rest
     assert fwd(lib, dt=-1) == INVALID
     assert fwd(lib, mode=2) == INVALID
@@ -205,3 +207,21 @@ def test_public_names_resolve():
     for name in pkg.__all__:
         assert getattr(pkg, name) is not None, name
     from gated_linear_recurrence_chunked_amd import ESALayer, esa_scan, scan_fwd, state_step  # noqa: F401
+
+
+def test_force_timeout_flag_validation(lib):
+    """ESA_TEST_FORCE_TIMEOUT (0x200) is accepted by esa_scan_fwd and esa_scan_bwd for fp16
+    storage with Dh = 64 only, and rejected by the other calls; every check returns before
+    any launch (a valid flagged call here stops at the zero-byte workspace)."""
+    F = 0x200
+    assert fwd(lib, dt=1, Dh=64, mode=1 | F) == WORKSPACE
+    assert fwd(lib, dt=1, Dh=64, mode=0 | F | 0x100) == WORKSPACE
+    assert fwd(lib, dt=0, Dh=64, mode=1 | F) == UNSUPPORTED
+    assert fwd(lib, dt=2, Dh=64, mode=1 | F) == UNSUPPORTED
+    assert fwd(lib, dt=1, Dh=32, mode=1 | F) == UNSUPPORTED
+    p = [addr(k) for k in range(1, 6)]
+    assert lib.esa_state_step(4, 2, 64, 1, 1 | F, *p, None) == INVALID
+    assert lib.esa_scan_segment_fwd(2, 100, 2, 64, 1, 1 | F, addr(1), addr(2), addr(3), addr(4),
+                                    addr(5), 0, None) == INVALID
+    assert lib.esa_scan_segment_bwd(2, 100, 2, 64, 1, 1 | F, addr(1), addr(2), addr(3), None,
+                                    addr(4), None, addr(5), addr(6), 0, None) == INVALID

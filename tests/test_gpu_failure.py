@@ -1,9 +1,9 @@
-"""A look-back failure forced from the host, through the workspace header's test controls:
-the first tile of every chain withholds its published values (word 2) and the wait's poll
-limit is made small (word 1), so every wait on a withheld value ends by timing out.  The
-call still returns; the sticky abort word (word 3) is set; the outputs of the first tile
-are exact and every output that depends on the withheld values is NaN; re-initialising the
-workspace with esa_workspace_init restores normal runs."""
+"""A look-back failure forced from the host with the ESA_TEST_FORCE_TIMEOUT mode flag: the
+first tile of every chain withholds its published values and the wait's poll limit is
+small, so every wait on a withheld value ends by timing out.  The call still returns; the
+workspace's sticky abort word (word 3) is set; the outputs of the first tile are exact and
+every output that depends on the withheld values is NaN; re-initialising the workspace with
+esa_workspace_init restores normal runs."""
 import ctypes
 import sys
 
@@ -52,11 +52,10 @@ def test_withheld_first_tile_times_out_to_nan(det):
                           deterministic=True)
     ws = torch.zeros(binding.workspace_bytes(B, T, H, Dh, dt), dtype=torch.uint8, device=DEV)
 
-    # forward: the chain's first tile withholds; every later tile's carry is NaN
+    forced = binding.MODES[mode] | binding.TEST_FORCE_TIMEOUT
     h = header(ws)
-    h[1] = 4096
-    h[2] = 1
-    y, eT, ck = binding.scan_fwd(x["a"], x["v"], x["q"], mode=mode, return_ckpt=True,
+    # forward: the chain's first tile withholds; every later tile's carry is NaN
+    y, eT, ck = binding.scan_fwd(x["a"], x["v"], x["q"], mode=forced, return_ckpt=True,
                                  workspace=ws, deterministic=det)
     torch.cuda.synchronize()
     assert int(h[3]) != 0, "the abort word is set"
@@ -69,9 +68,7 @@ def test_withheld_first_tile_times_out_to_nan(det):
 
     # backward (from the good checkpoint): the chain starts at the last tile
     h.zero_()
-    h[1] = 4096
-    h[2] = 1
-    da, dv, dq, de0 = binding.scan_bwd(x["a"], x["v"], x["q"], x["dy"], ckpt=ck0, mode=mode,
+    da, dv, dq, de0 = binding.scan_bwd(x["a"], x["v"], x["q"], x["dy"], ckpt=ck0, mode=forced,
                                        workspace=ws, deterministic=det)
     torch.cuda.synchronize()
     assert int(h[3]) != 0
