@@ -240,7 +240,10 @@ def bench_decode(args, torch, binding, synth):
     res["decode_graph_steps_per_s"] = n / (gms * 1e-3)
     del graph
     res["decode_tokens_per_s"] = res["decode_steps_per_s"] * B
+    res["decode_graph_tokens_per_s"] = res["decode_graph_steps_per_s"] * B
     res["decode_step_bytes"] = B * H * Dh * (4 * 2 + 2 * 4)
+    # effective rate of a graph-replayed step (launch-bound: far below the HBM roofline)
+    res["decode_graph_GB_s"] = res["decode_step_bytes"] / (res["decode_graph_us_per_step"] * 1e-6) / 1e9
     return res
 
 
