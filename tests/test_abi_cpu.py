@@ -225,3 +225,11 @@ def test_force_timeout_flag_validation(lib):
                                     addr(5), 0, None) == INVALID
     assert lib.esa_scan_segment_bwd(2, 100, 2, 64, 1, 1 | F, addr(1), addr(2), addr(3), None,
                                     addr(4), None, addr(5), addr(6), 0, None) == INVALID
+
+
+def test_torch_step_binding_loads():
+    """The decode step's torch-tensor call path (_esa_torch, built beside libesa.so) imports
+    without a GPU and exposes state_step."""
+    from gated_linear_recurrence_chunked_amd import _esa_torch
+
+    assert callable(_esa_torch.state_step)
