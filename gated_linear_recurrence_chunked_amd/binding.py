@@ -16,9 +16,10 @@ Sequence segments (the scan over T cut into consecutive pieces, e.g. one per dev
     seg_d_init = segment_bwd(a_k, v_k, q_k, dy_k, carry[k], ckpt_k)
     dcarry, d_init = segment_compose(P_all, D_all, d_final_state, reverse=True)
 
-The decode step (state_step, StepPlan) goes through _esa_torch, a small C++ binding of
-esa_state_step built beside libesa.so that takes torch tensors directly; every other call
-goes through ctypes.
+scan_fwd, scan_bwd, state_step and StepPlan go through _esa_torch, a small C++ binding of
+the same C ABI built beside libesa.so that takes torch tensors directly (a few microseconds
+of host time a call, against 5-17 us through ctypes with the checks in Python); the segment
+calls and the size queries go through ctypes.
 
 Sequence tensors are [B, T, H, Dh] (fp32, fp16, bf16, or the OCP 8-bit formats
 float8_e4m3fn / float8_e5m2; one dtype per call); states are fp32 [B, H, Dh].
@@ -73,14 +74,15 @@ def library_path() -> str:
     return os.path.join(_HERE, LIB_NAME)
 
 
-_step_ext = None
+_ext = None
 
 
-def _torch_step():
-    """The decode step's torch-tensor call path (_esa_torch, built beside libesa.so): the same
-    esa_state_step, without ctypes marshalling.  Raises if it has not been built."""
-    global _step_ext
-    if _step_ext is None:
+def _torch_ext():
+    """The torch-tensor call path of esa_scan_fwd, esa_scan_bwd and esa_state_step
+    (_esa_torch, built beside libesa.so): the same C ABI without ctypes marshalling.
+    Raises if it has not been built."""
+    global _ext
+    if _ext is None:
         load_library()
         try:
             from . import _esa_torch
@@ -88,8 +90,8 @@ def _torch_step():
             raise RuntimeError(
                 "the _esa_torch extension is missing: build it with "
                 "`python -m gated_linear_recurrence_chunked_amd.build`") from e
-        _step_ext = _esa_torch.state_step
-    return _step_ext
+        _ext = _esa_torch
+    return _ext
 
 
 def load_library():
@@ -206,47 +208,51 @@ def get_workspace(nbytes: int, device) -> torch.Tensor:
     The library leaves a workspace ready for reuse after every call, so the cache only
     zero-fills on allocation.  One workspace per stream: calls on one stream are ordered.
     """
-    dev = torch.device(device)
-    if dev.index is None:
-        dev = torch.device("cuda", torch.cuda.current_device())
-    key = (dev.index, _raw_stream(dev.index))
+    if isinstance(device, int):
+        index = device
+    else:
+        dev = torch.device(device)
+        index = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (index, _raw_stream(index))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=torch.device("cuda", index))
         _workspaces[key] = ws
     return ws
+
+
+_ws_need: dict = {}
+
+
+def _workspace_for(a) -> torch.Tensor:
+    """The cached workspace for a scan over the gate logits `a` ([B, T, H, Dh]); the size
+    query runs once per shape and dtype."""
+    if not isinstance(a, torch.Tensor) or not a.is_cuda:
+        raise TypeError("gate_logit must be a CUDA (HIP) tensor")
+    if a.dim() != 4:
+        raise ValueError(f"gate_logit must be [B, T, H, Dh], got {tuple(a.shape)}")
+    key = (a.shape, a.dtype)
+    need = _ws_need.get(key)
+    if need is None:
+        if a.dtype not in DTYPES:
+            raise TypeError(f"gate_logit: dtype {a.dtype} not supported")
+        need = workspace_bytes(*a.shape, a.dtype)
+        _ws_need[key] = need
+    return get_workspace(need, a.get_device())
 
 
 def scan_fwd(a, v, q, init_state=None, mode="controlled", return_ckpt=False, final_state=None,
              y=None, workspace=None, deterministic=False):
     """Forward scan with fused gate and readout (esa_scan_fwd).  deterministic=True makes the
-    result bitwise reproducible (ESA_DETERMINISTIC)."""
-    lib = load_library()
-    a = _seq("gate_logit", a)
-    v = _seq("value", v, a)
-    q = _seq("query", q, a)
-    B, T, H, Dh = a.shape
-    init_state = _state("init_state", init_state, B, H, Dh, a.device)
-    if y is None:
-        y = torch.empty_like(a)
-    else:
-        _out("y", y, a.shape, a.dtype, a.device)
-    if final_state is None:
-        final_state = torch.empty((B, H, Dh), dtype=torch.float32, device=a.device)
-    else:
-        _out("final_state", final_state, (B, H, Dh), torch.float32, a.device)
-    ckpt = None
-    if return_ckpt:
-        nck = max(1, ckpt_bytes(B, T, H, Dh) // 4)
-        ckpt = torch.empty(nck, dtype=torch.float32, device=a.device)
-    need = workspace_bytes(B, T, H, Dh, a.dtype)
-    ws = workspace if workspace is not None else get_workspace(need, a.device)
-    with _OnDevice(a.device.index):
-        st = lib.esa_scan_fwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode, deterministic), _ptr(a),
-                              _ptr(v), _ptr(q),
-                              _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(ckpt), _ptr(ws),
-                              ws.numel() * ws.element_size(), _stream_handle(a.device))
-    _check(st, "esa_scan_fwd")
+    result bitwise reproducible (ESA_DETERMINISTIC).  Sequence inputs are made contiguous;
+    caller-provided outputs (y, final_state) must already be contiguous and of the right
+    shape, dtype and device."""
+    ext = _ext if _ext is not None else _torch_ext()
+    ws = workspace if workspace is not None else _workspace_for(a)
+    st, y, final_state, ckpt = ext.scan_fwd(a, v, q, init_state, _mode(mode, deterministic),
+                                            bool(return_ckpt), final_state, y, ws)
+    if st:
+        _check(st, "esa_scan_fwd")
     if return_ckpt:
         return y, final_state, ckpt
     return y, final_state
@@ -257,39 +263,13 @@ def scan_bwd(a, v, q, dy, init_state=None, d_final_state=None, ckpt=None, mode="
              d_init=None):
     """Backward of scan_fwd (esa_scan_bwd).  Returns (d_logit, d_value, d_query, d_init);
     any of the four may be passed in to be written in place."""
-    lib = load_library()
-    a = _seq("gate_logit", a)
-    v = _seq("value", v, a)
-    q = _seq("query", q, a)
-    dy = _seq("dy", dy, a)
-    B, T, H, Dh = a.shape
-    init_state = _state("init_state", init_state, B, H, Dh, a.device)
-    d_final_state = _state("d_final_state", d_final_state, B, H, Dh, a.device)
-    if ckpt is not None:
-        if ckpt.dtype != torch.float32 or ckpt.numel() * 4 < ckpt_bytes(B, T, H, Dh):
-            raise ValueError("ckpt must be the fp32 checkpoint of scan_fwd(return_ckpt=True)")
-        ckpt = ckpt.contiguous()
-    grads = []
-    for name, t in (("d_logit", d_logit), ("d_value", d_value), ("d_query", d_query)):
-        if t is None:
-            t = torch.empty_like(a)
-        else:
-            _out(name, t, a.shape, a.dtype, a.device)
-        grads.append(t)
-    da, dv, dq = grads
-    if d_init is None:
-        d_init = torch.empty((B, H, Dh), dtype=torch.float32, device=a.device)
-    else:
-        _out("d_init", d_init, (B, H, Dh), torch.float32, a.device)
-    need = workspace_bytes(B, T, H, Dh, a.dtype)
-    ws = workspace if workspace is not None else get_workspace(need, a.device)
-    with _OnDevice(a.device.index):
-        st = lib.esa_scan_bwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode, deterministic), _ptr(a),
-                              _ptr(v), _ptr(q),
-                              _ptr(init_state), _ptr(dy), _ptr(d_final_state), _ptr(ckpt),
-                              _ptr(da), _ptr(dv), _ptr(dq), _ptr(d_init), _ptr(ws),
-                              ws.numel() * ws.element_size(), _stream_handle(a.device))
-    _check(st, "esa_scan_bwd")
+    ext = _ext if _ext is not None else _torch_ext()
+    ws = workspace if workspace is not None else _workspace_for(a)
+    st, da, dv, dq, d_init = ext.scan_bwd(a, v, q, dy, init_state, d_final_state, ckpt,
+                                          _mode(mode, deterministic), ws, d_logit, d_value,
+                                          d_query, d_init)
+    if st:
+        _check(st, "esa_scan_bwd")
     return da, dv, dq, d_init
 
 
@@ -297,7 +277,7 @@ def state_step(a, v, q, state, mode="controlled", y=None):
     """One-token update (esa_state_step): `state` (fp32 [B, H, Dh]) is updated in place.
     The tensors' shapes, dtypes, devices and layout are checked in the _esa_torch call path
     (ValueError on a mismatch)."""
-    step = _step_ext if _step_ext is not None else _torch_step()
+    ext = _ext if _ext is not None else _torch_ext()
     for name, t in (("gate_logit", a), ("value", v), ("query", q), ("state", state)):
         if not isinstance(t, torch.Tensor):
             raise ValueError(f"{name} must be a tensor")
@@ -305,7 +285,10 @@ def state_step(a, v, q, state, mode="controlled", y=None):
         y = torch.empty_like(a)
     elif not isinstance(y, torch.Tensor):
         raise ValueError("y must be a tensor")
-    return step(state, a, v, q, y, _mode(mode))
+    st = ext.state_step(state, a, v, q, y, _mode(mode))
+    if st:
+        _check(st, "esa_state_step")
+    return y
 
 
 def segment_fwd(a, v, mode="controlled", workspace=None, deterministic=False):
@@ -400,7 +383,7 @@ class StepPlan:
             raise ValueError("state must be a contiguous fp32 [B, H, Dh] CUDA (HIP) tensor")
         if dtype not in DTYPES:
             raise TypeError(f"dtype {dtype} not supported")
-        self._step = _torch_step()
+        self._step = _torch_ext().state_step
         self.state = state
         self.shape = state.shape
         self.dtype = dtype
@@ -412,4 +395,7 @@ class StepPlan:
         # dtype and a contiguous layout; the plan adds only its own dtype
         if a.dtype is not self.dtype:
             raise ValueError(f"step tensors must be {self.dtype}, got {a.dtype}")
-        return self._step(self.state, a, v, q, y, self._mode)
+        st = self._step(self.state, a, v, q, y, self._mode)
+        if st:
+            _check(st, "esa_state_step")
+        return y

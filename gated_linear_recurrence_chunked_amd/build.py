@@ -27,7 +27,7 @@ ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
-TORCH_EXT = "esa_torch_step.cpp"  # the torch-tensor binding of esa_state_step
+TORCH_EXT = "esa_torch.cpp"  # the torch-tensor call path of the scans and the step
 TORCH_MOD = "_esa_torch"
 
 # -packed-fp32-ops: never emit packed fp32 arithmetic (v_pk_*_f32); plain fp32 ops only.
@@ -63,7 +63,7 @@ def _torch_paths():
 
 def _compile_torch_ext() -> str:
     inc, _, _, abi = _torch_paths()
-    obj = os.path.join(BUILD, "esa_torch_step.o")
+    obj = os.path.join(BUILD, "esa_torch.o")
     cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
            f"-DTORCH_EXTENSION_NAME={TORCH_MOD}", f"-D_GLIBCXX_USE_CXX11_ABI={abi}",
            "-I", INCLUDE, "-I", os.path.join(ROCM, "include")]
