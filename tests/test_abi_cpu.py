@@ -227,9 +227,10 @@ def test_force_timeout_flag_validation(lib):
                                     addr(4), None, addr(5), addr(6), 0, None) == INVALID
 
 
-def test_torch_step_binding_loads():
-    """The decode step's torch-tensor call path (_esa_torch, built beside libesa.so) imports
-    without a GPU and exposes state_step."""
+def test_torch_call_path_loads():
+    """The torch-tensor call path (_esa_torch, built beside libesa.so) imports without a GPU
+    and exposes the scans and the step."""
     from gated_linear_recurrence_chunked_amd import _esa_torch
 
-    assert callable(_esa_torch.state_step)
+    for name in ("scan_fwd", "scan_bwd", "state_step"):
+        assert callable(getattr(_esa_torch, name))
