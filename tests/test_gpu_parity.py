@@ -276,6 +276,23 @@ def test_binding_rejects_mismatched_outputs():
     for g_, o_, r_ in zip(got, outs, ref):
         assert g_ is o_
         assert torch.equal(g_, r_)
+    # mismatched sequence inputs are refused; non-contiguous ones are taken as their values
+    with pytest.raises(TypeError):
+        binding.scan_fwd(x["a"], x["v"].cpu(), x["q"])
+    with pytest.raises(ValueError):
+        binding.scan_fwd(x["a"], x["v"][:, :-1], x["q"][:, :-1])
+    with pytest.raises(ValueError):
+        binding.scan_fwd(x["a"], x["v"].float(), x["q"])
+    with pytest.raises(ValueError):
+        binding.scan_bwd(x["a"], x["v"], x["q"], dy, ckpt=ck.half())
+    with pytest.raises(ValueError):
+        binding.scan_fwd(x["a"], x["v"], x["q"], init_state=torch.zeros(B, H, Dh + 1, device=DEV))
+    vt = x["v"].transpose(1, 2).contiguous().transpose(1, 2)  # same values, strided
+    assert not vt.is_contiguous()
+    y1, e1 = binding.scan_fwd(x["a"], x["v"], x["q"], deterministic=True)
+    y2, e2 = binding.scan_fwd(x["a"], vt, x["q"], deterministic=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(e1, e2)
 
 
 def test_saturated_gates_reach_special_cases():
