@@ -302,6 +302,8 @@ def segment_fwd(a, v, mode="controlled", workspace=None, deterministic=False):
     seg_prod = torch.empty_like(seg_state)
     need = workspace_bytes(B, T, H, Dh, a.dtype)
     ws = workspace if workspace is not None else get_workspace(need, a.device)
+    if ws.device != a.device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {a.device}")
     with _OnDevice(a.device.index):
         st = lib.esa_scan_segment_fwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode, deterministic),
                                       _ptr(a), _ptr(v),
@@ -323,12 +325,15 @@ def segment_bwd(a, v, q, dy, init_state=None, ckpt=None, mode="controlled", work
     B, T, H, Dh = a.shape
     init_state = _state("init_state", init_state, B, H, Dh, a.device)
     if ckpt is not None:
-        if ckpt.dtype != torch.float32 or ckpt.numel() * 4 < ckpt_bytes(B, T, H, Dh):
+        if (ckpt.dtype != torch.float32 or ckpt.device != a.device
+                or ckpt.numel() * 4 < ckpt_bytes(B, T, H, Dh)):
             raise ValueError("ckpt must be the fp32 checkpoint of scan_fwd(return_ckpt=True)")
         ckpt = ckpt.contiguous()
     seg_d_init = torch.empty((B, H, Dh), dtype=torch.float32, device=a.device)
     need = workspace_bytes(B, T, H, Dh, a.dtype)
     ws = workspace if workspace is not None else get_workspace(need, a.device)
+    if ws.device != a.device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {a.device}")
     with _OnDevice(a.device.index):
         st = lib.esa_scan_segment_bwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode, deterministic),
                                       _ptr(a), _ptr(v),

@@ -65,6 +65,12 @@ void out(const char* name, const at::Tensor& t, at::IntArrayRef shape, at::Scala
 
 const void* ptr(const c10::optional<at::Tensor>& t) { return t.has_value() ? t->data_ptr() : nullptr; }
 
+// The workspace (any dtype; its bytes count) must be device memory of the inputs' device.
+void check_workspace(const at::Tensor& ws, const c10::Device& dev) {
+    TORCH_CHECK_VALUE(ws.device() == dev && ws.is_contiguous(),
+                      "workspace must be a contiguous tensor on ", dev);
+}
+
 // esa_scan_fwd.  Returns (status, y, final_state, ckpt or None).
 std::tuple<int64_t, at::Tensor, at::Tensor, c10::optional<at::Tensor>> scan_fwd(
     const at::Tensor& a_, const at::Tensor& v_, const at::Tensor& q_,
@@ -85,6 +91,7 @@ std::tuple<int64_t, at::Tensor, at::Tensor, c10::optional<at::Tensor>> scan_fwd(
         out("final_state", *final_state, sshape, at::kFloat, dev);
     else
         final_state = at::empty(sshape, a.options().dtype(at::kFloat));
+    check_workspace(workspace, dev);
     c10::optional<at::Tensor> ckpt;
     if (return_ckpt) {
         const int64_t n = std::max<int64_t>(1, (int64_t)(esa_scan_ckpt_bytes(B, T, H, Dh) / 4));
@@ -116,9 +123,10 @@ std::tuple<int64_t, at::Tensor, at::Tensor, at::Tensor, at::Tensor> scan_bwd(
     const std::vector<int64_t> sshape{B, H, Dh};
     const auto init_state = state("init_state", init_state_, sshape, dev);
     const auto d_final = state("d_final_state", d_final_, sshape, dev);
+    check_workspace(workspace, dev);
     c10::optional<at::Tensor> ckpt;
     if (ckpt_.has_value()) {
-        TORCH_CHECK_VALUE(ckpt_->scalar_type() == at::kFloat &&
+        TORCH_CHECK_VALUE(ckpt_->scalar_type() == at::kFloat && ckpt_->device() == dev &&
                               (size_t)ckpt_->numel() * 4 >= esa_scan_ckpt_bytes(B, T, H, Dh),
                           "ckpt must be the fp32 checkpoint of scan_fwd(return_ckpt=True)");
         ckpt = ckpt_->contiguous();

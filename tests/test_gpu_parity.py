@@ -287,6 +287,18 @@ def test_binding_rejects_mismatched_outputs():
         binding.scan_bwd(x["a"], x["v"], x["q"], dy, ckpt=ck.half())
     with pytest.raises(ValueError):
         binding.scan_fwd(x["a"], x["v"], x["q"], init_state=torch.zeros(B, H, Dh + 1, device=DEV))
+    # host memory where device memory is needed is refused before any launch
+    host_ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        binding.scan_fwd(x["a"], x["v"], x["q"], workspace=host_ws)
+    with pytest.raises(ValueError):
+        binding.scan_bwd(x["a"], x["v"], x["q"], dy, ckpt=ck, workspace=host_ws)
+    with pytest.raises(ValueError):
+        binding.scan_bwd(x["a"], x["v"], x["q"], dy, ckpt=ck.cpu())
+    with pytest.raises(ValueError):
+        binding.segment_fwd(x["a"], x["v"], workspace=host_ws)
+    with pytest.raises(ValueError):
+        binding.segment_bwd(x["a"], x["v"], x["q"], dy, ckpt=ck.cpu())
     vt = x["v"].transpose(1, 2).contiguous().transpose(1, 2)  # same values, strided
     assert not vt.is_contiguous()
     y1, e1 = binding.scan_fwd(x["a"], x["v"], x["q"], deterministic=True)
