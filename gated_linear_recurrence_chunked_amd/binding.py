@@ -1,4 +1,4 @@
-"""ctypes binding of libesa.so (include/esa.h), with torch for device memory and streams.
+"""Python binding of libesa.so (include/esa.h), with torch for device memory and streams.
 
 Argument marshalling only: every step of the computation runs in the library's HIP
 kernels.  When the library is missing, every call raises; there is no fallback path.
@@ -16,10 +16,10 @@ Sequence segments (the scan over T cut into consecutive pieces, e.g. one per dev
     seg_d_init = segment_bwd(a_k, v_k, q_k, dy_k, carry[k], ckpt_k)
     dcarry, d_init = segment_compose(P_all, D_all, d_final_state, reverse=True)
 
-scan_fwd, scan_bwd, state_step and StepPlan go through _esa_torch, a small C++ binding of
-the same C ABI built beside libesa.so that takes torch tensors directly (a few microseconds
-of host time a call, against 5-17 us through ctypes with the checks in Python); the segment
-calls and the size queries go through ctypes.
+Every call goes through _esa_torch, a small C++ binding of the same C ABI built beside
+libesa.so that takes torch tensors directly and checks them there (a few microseconds of
+host time a call, against 5-17 us through ctypes with the checks in Python); ctypes loads
+libesa.so for the size queries and the status strings.
 
 Sequence tensors are [B, T, H, Dh] (fp32, fp16, bf16, or the OCP 8-bit formats
 float8_e4m3fn / float8_e5m2; one dtype per call); states are fp32 [B, H, Dh].
@@ -125,73 +125,15 @@ def _check(status: int, where: str):
         raise EsaError(status, where)
 
 
-def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
-
-
 def _raw_stream(index: int) -> int:
     """The current HIP stream of device `index` as an integer handle (torch's raw accessor,
-    without building a Python stream object: a decode step calls this once per token)."""
+    without building a Python stream object)."""
     return torch._C._cuda_getCurrentRawStream(index)
-
-
-def _stream_handle(device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(_raw_stream(device.index))
-
-
-class _OnDevice:
-    """Makes `index` the current device for the call, and skips the switch when it already
-    is (the common case; a device switch costs more host time than a decode step's launch)."""
-    __slots__ = ("index", "prev")
-
-    def __init__(self, index: int):
-        self.index = index
-        self.prev = None
-
-    def __enter__(self):
-        cur = torch._C._cuda_getDevice()
-        if cur != self.index:
-            self.prev = cur
-            torch._C._cuda_setDevice(self.index)
-
-    def __exit__(self, *exc):
-        if self.prev is not None:
-            torch._C._cuda_setDevice(self.prev)
-        return False
 
 
 def _mode(mode, deterministic=False) -> int:
     m = MODES[mode] if isinstance(mode, str) else int(mode)
     return m | DETERMINISTIC if deterministic else m
-
-
-def _seq(name, t, like=None):
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
-    if t.dim() != 4:
-        raise ValueError(f"{name} must be [B, T, H, Dh], got {tuple(t.shape)}")
-    if t.dtype not in DTYPES:
-        raise TypeError(f"{name}: dtype {t.dtype} not supported")
-    if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device):
-        raise ValueError(f"{name} must match shape/dtype/device of the gate logits")
-    return t.contiguous()
-
-
-def _state(name, t, B, H, Dh, device):
-    if t is None:
-        return None
-    if t.dtype != torch.float32 or tuple(t.shape) != (B, H, Dh) or t.device != device:
-        raise ValueError(f"{name} must be fp32 [B, H, Dh] = {(B, H, Dh)} on {device}")
-    return t.contiguous()
-
-
-def _out(name, t, shape, dtype, device):
-    """A caller-provided output is written in place, so it must already be what the library
-    writes: contiguous, of the given shape, dtype and device (no copy is made)."""
-    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype
-            or t.device != device or not t.is_contiguous()):
-        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
-                         f"on {device}")
 
 
 def workspace_bytes(B, T, H, Dh, dtype) -> int:
@@ -294,22 +236,11 @@ def state_step(a, v, q, state, mode="controlled", y=None):
 def segment_fwd(a, v, mode="controlled", workspace=None, deterministic=False):
     """Aggregate of one sequence segment from a zero state (esa_scan_segment_fwd): returns
     (seg_state, seg_gate_prod), fp32 [B, H, Dh] each."""
-    lib = load_library()
-    a = _seq("gate_logit", a)
-    v = _seq("value", v, a)
-    B, T, H, Dh = a.shape
-    seg_state = torch.empty((B, H, Dh), dtype=torch.float32, device=a.device)
-    seg_prod = torch.empty_like(seg_state)
-    need = workspace_bytes(B, T, H, Dh, a.dtype)
-    ws = workspace if workspace is not None else get_workspace(need, a.device)
-    if ws.device != a.device or not ws.is_contiguous():
-        raise ValueError(f"workspace must be a contiguous tensor on {a.device}")
-    with _OnDevice(a.device.index):
-        st = lib.esa_scan_segment_fwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode, deterministic),
-                                      _ptr(a), _ptr(v),
-                                      _ptr(seg_state), _ptr(seg_prod), _ptr(ws),
-                                      ws.numel() * ws.element_size(), _stream_handle(a.device))
-    _check(st, "esa_scan_segment_fwd")
+    ext = _ext if _ext is not None else _torch_ext()
+    ws = workspace if workspace is not None else _workspace_for(a)
+    st, seg_state, seg_prod = ext.segment_fwd(a, v, _mode(mode, deterministic), ws)
+    if st:
+        _check(st, "esa_scan_segment_fwd")
     return seg_state, seg_prod
 
 
@@ -317,30 +248,12 @@ def segment_bwd(a, v, q, dy, init_state=None, ckpt=None, mode="controlled", work
                 deterministic=False):
     """Gradient reaching a segment's initial state with none arriving at its end
     (esa_scan_segment_bwd): fp32 [B, H, Dh]."""
-    lib = load_library()
-    a = _seq("gate_logit", a)
-    v = _seq("value", v, a)
-    q = _seq("query", q, a)
-    dy = _seq("dy", dy, a)
-    B, T, H, Dh = a.shape
-    init_state = _state("init_state", init_state, B, H, Dh, a.device)
-    if ckpt is not None:
-        if (ckpt.dtype != torch.float32 or ckpt.device != a.device
-                or ckpt.numel() * 4 < ckpt_bytes(B, T, H, Dh)):
-            raise ValueError("ckpt must be the fp32 checkpoint of scan_fwd(return_ckpt=True)")
-        ckpt = ckpt.contiguous()
-    seg_d_init = torch.empty((B, H, Dh), dtype=torch.float32, device=a.device)
-    need = workspace_bytes(B, T, H, Dh, a.dtype)
-    ws = workspace if workspace is not None else get_workspace(need, a.device)
-    if ws.device != a.device or not ws.is_contiguous():
-        raise ValueError(f"workspace must be a contiguous tensor on {a.device}")
-    with _OnDevice(a.device.index):
-        st = lib.esa_scan_segment_bwd(B, T, H, Dh, DTYPES[a.dtype], _mode(mode, deterministic),
-                                      _ptr(a), _ptr(v),
-                                      _ptr(q), _ptr(init_state), _ptr(dy), _ptr(ckpt),
-                                      _ptr(seg_d_init), _ptr(ws), ws.numel() * ws.element_size(),
-                                      _stream_handle(a.device))
-    _check(st, "esa_scan_segment_bwd")
+    ext = _ext if _ext is not None else _torch_ext()
+    ws = workspace if workspace is not None else _workspace_for(a)
+    st, seg_d_init = ext.segment_bwd(a, v, q, dy, init_state, ckpt, _mode(mode, deterministic),
+                                     ws)
+    if st:
+        _check(st, "esa_scan_segment_bwd")
     return seg_d_init
 
 
@@ -348,25 +261,13 @@ def segment_compose(seg_gate_prod, seg_agg, boundary=None, reverse=False):
     """Compose segment aggregates (esa_segment_compose).  seg_gate_prod, seg_agg: fp32
     [nseg, B, H, Dh]; boundary: fp32 [B, H, Dh] or None.  Returns (carry [nseg, B, H, Dh],
     total [B, H, Dh])."""
-    lib = load_library()
+    ext = _ext if _ext is not None else _torch_ext()
     for name, t in (("seg_gate_prod", seg_gate_prod), ("seg_agg", seg_agg)):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32:
+        if not isinstance(t, torch.Tensor):
             raise ValueError(f"{name} must be an fp32 CUDA (HIP) tensor")
-    if seg_agg.shape != seg_gate_prod.shape or seg_agg.device != seg_gate_prod.device:
-        raise ValueError("seg_gate_prod and seg_agg must share shape and device")
-    p = seg_gate_prod.contiguous()
-    x = seg_agg.contiguous()
-    nseg = p.shape[0]
-    lanes = p[0].numel()
-    if boundary is not None:
-        _out("boundary", boundary, p.shape[1:], torch.float32, p.device)
-    carry = torch.empty_like(p)
-    total = torch.empty(p.shape[1:], dtype=torch.float32, device=p.device)
-    with _OnDevice(p.device.index):
-        st = lib.esa_segment_compose(nseg, lanes, 1 if reverse else 0, _ptr(p), _ptr(x),
-                                     _ptr(boundary), _ptr(carry), _ptr(total),
-                                     _stream_handle(p.device))
-    _check(st, "esa_segment_compose")
+    st, carry, total = ext.segment_compose(seg_gate_prod, seg_agg, boundary, bool(reverse))
+    if st:
+        _check(st, "esa_segment_compose")
     return carry, total
 
 

@@ -1,8 +1,8 @@
-// The library's hot calls from Python without ctypes: torch tensors in, the C ABI out.
+// The library's calls from Python without ctypes: torch tensors in, the C ABI out.
 // Argument marshalling only: the checks the Python binding documents (shapes, dtypes,
 // devices, layouts), output allocation, the current HIP stream of the tensors' device; the
-// computation is the library's kernels behind esa_scan_fwd, esa_scan_bwd and
-// esa_state_step.  Through ctypes with the checks in Python a call cost 10 us (forward),
+// computation is the library's kernels behind esa_scan_fwd, esa_scan_bwd, esa_state_step
+// and the sequence-segment calls.  Through ctypes with the checks in Python a call cost 10 us (forward),
 // 17 us (backward) and 5-7 us (decode step) of host time, more than the kernels of small
 // problems take; here it is a few microseconds.
 //
@@ -154,6 +154,84 @@ std::tuple<int64_t, at::Tensor, at::Tensor, at::Tensor, at::Tensor> scan_bwd(
     return {st, *da, *dv, *dq, *d_init};
 }
 
+// esa_scan_segment_fwd.  Returns (status, seg_state, seg_gate_prod).
+std::tuple<int64_t, at::Tensor, at::Tensor> segment_fwd(const at::Tensor& a_, const at::Tensor& v_,
+                                                        int64_t mode, at::Tensor workspace) {
+    const at::Tensor a = seq("gate_logit", a_, nullptr);
+    const at::Tensor v = seq("value", v_, &a);
+    const int64_t B = a.size(0), T = a.size(1), H = a.size(2), Dh = a.size(3);
+    const c10::Device dev = a.device();
+    check_workspace(workspace, dev);
+    const auto opts = a.options().dtype(at::kFloat);
+    at::Tensor seg_state = at::empty({B, H, Dh}, opts), seg_prod = at::empty({B, H, Dh}, opts);
+    const c10::hip::HIPGuard guard(dev.index());
+    const hipStream_t s = c10::hip::getCurrentHIPStream(dev.index()).stream();
+    const int st = esa_scan_segment_fwd(B, T, H, Dh, dtype_code(a.scalar_type()), (int)mode,
+                                        a.data_ptr(), v.data_ptr(), seg_state.data_ptr<float>(),
+                                        seg_prod.data_ptr<float>(), workspace.data_ptr(),
+                                        workspace.nbytes(), s);
+    return {st, seg_state, seg_prod};
+}
+
+// esa_scan_segment_bwd.  Returns (status, seg_d_init).
+std::tuple<int64_t, at::Tensor> segment_bwd(const at::Tensor& a_, const at::Tensor& v_,
+                                            const at::Tensor& q_, const at::Tensor& dy_,
+                                            const c10::optional<at::Tensor>& init_state_,
+                                            const c10::optional<at::Tensor>& ckpt_, int64_t mode,
+                                            at::Tensor workspace) {
+    const at::Tensor a = seq("gate_logit", a_, nullptr);
+    const at::Tensor v = seq("value", v_, &a);
+    const at::Tensor q = seq("query", q_, &a);
+    const at::Tensor dy = seq("dy", dy_, &a);
+    const int64_t B = a.size(0), T = a.size(1), H = a.size(2), Dh = a.size(3);
+    const c10::Device dev = a.device();
+    const std::vector<int64_t> sshape{B, H, Dh};
+    const auto init_state = state("init_state", init_state_, sshape, dev);
+    check_workspace(workspace, dev);
+    c10::optional<at::Tensor> ckpt;
+    if (ckpt_.has_value()) {
+        TORCH_CHECK_VALUE(ckpt_->scalar_type() == at::kFloat && ckpt_->device() == dev &&
+                              (size_t)ckpt_->numel() * 4 >= esa_scan_ckpt_bytes(B, T, H, Dh),
+                          "ckpt must be the fp32 checkpoint of scan_fwd(return_ckpt=True)");
+        ckpt = ckpt_->contiguous();
+    }
+    at::Tensor seg_d_init = at::empty(sshape, a.options().dtype(at::kFloat));
+    const c10::hip::HIPGuard guard(dev.index());
+    const hipStream_t s = c10::hip::getCurrentHIPStream(dev.index()).stream();
+    const int st = esa_scan_segment_bwd(
+        B, T, H, Dh, dtype_code(a.scalar_type()), (int)mode, a.data_ptr(), v.data_ptr(),
+        q.data_ptr(), static_cast<const float*>(ptr(init_state)), dy.data_ptr(),
+        static_cast<const float*>(ptr(ckpt)), seg_d_init.data_ptr<float>(), workspace.data_ptr(),
+        workspace.nbytes(), s);
+    return {st, seg_d_init};
+}
+
+// esa_segment_compose over fp32 [nseg, B, H, Dh] stacks.  Returns (status, carry, total).
+std::tuple<int64_t, at::Tensor, at::Tensor> segment_compose(const at::Tensor& prod_,
+                                                            const at::Tensor& agg_,
+                                                            const c10::optional<at::Tensor>& boundary,
+                                                            bool reverse) {
+    for (const at::Tensor* t : {&prod_, &agg_})
+        TORCH_CHECK_VALUE(t->is_cuda() && t->scalar_type() == at::kFloat && t->dim() >= 1,
+                          "seg_gate_prod and seg_agg must be fp32 CUDA (HIP) tensors");
+    TORCH_CHECK_VALUE(agg_.sizes() == prod_.sizes() && agg_.device() == prod_.device(),
+                      "seg_gate_prod and seg_agg must share shape and device");
+    const at::Tensor p = prod_.contiguous(), x = agg_.contiguous();
+    const c10::Device dev = p.device();
+    const at::IntArrayRef lane_shape = p.sizes().slice(1);
+    if (boundary.has_value()) out("boundary", *boundary, lane_shape, at::kFloat, dev);
+    at::Tensor carry = at::empty_like(p);
+    at::Tensor total = at::empty(lane_shape, p.options());
+    const int64_t nseg = p.size(0), lanes = nseg ? p.numel() / nseg : 0;
+    const c10::hip::HIPGuard guard(dev.index());
+    const hipStream_t s = c10::hip::getCurrentHIPStream(dev.index()).stream();
+    const int st = esa_segment_compose(nseg, lanes, reverse ? 1 : 0, p.data_ptr<float>(),
+                                       x.data_ptr<float>(),
+                                       static_cast<const float*>(ptr(boundary)),
+                                       carry.data_ptr<float>(), total.data_ptr<float>(), s);
+    return {st, carry, total};
+}
+
 // esa_state_step: state (fp32 [B, H, Dh], in place) and y ([B, H, Dh], written) from this
 // token's gate logits a, values v and queries q ([B, H, Dh], one storage dtype).  Mismatched
 // arguments raise ValueError.  Returns the library's status.
@@ -184,4 +262,7 @@ PYBIND11_MODULE(TORCH_EXTENSION_NAME, m) {
     m.def("scan_fwd", &scan_fwd, "esa_scan_fwd on torch tensors (see include/esa.h)");
     m.def("scan_bwd", &scan_bwd, "esa_scan_bwd on torch tensors (see include/esa.h)");
     m.def("state_step", &state_step, "esa_state_step on torch tensors (see include/esa.h)");
+    m.def("segment_fwd", &segment_fwd, "esa_scan_segment_fwd on torch tensors");
+    m.def("segment_bwd", &segment_bwd, "esa_scan_segment_bwd on torch tensors");
+    m.def("segment_compose", &segment_compose, "esa_segment_compose on torch tensors");
 }
