@@ -229,8 +229,9 @@ def test_force_timeout_flag_validation(lib):
 
 def test_torch_call_path_loads():
     """The torch-tensor call path (_esa_torch, built beside libesa.so) imports without a GPU
-    and exposes the scans and the step."""
+    and exposes every call of the binding."""
     from gated_linear_recurrence_chunked_amd import _esa_torch
 
-    for name in ("scan_fwd", "scan_bwd", "state_step"):
+    for name in ("scan_fwd", "scan_bwd", "state_step", "segment_fwd", "segment_bwd",
+                 "segment_compose"):
         assert callable(getattr(_esa_torch, name))
