@@ -66,9 +66,10 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="0 = min(16, cpu count)")
-    ap.add_argument("--only", choices=["train", "decode", "all", "copy", "workloads"],
+    ap.add_argument("--only", choices=["train", "decode", "variants", "all", "copy", "workloads"],
                     default="all",
                     help="copy: a plain 4 GiB device copy, the reference for HBM counters; "
+                         "variants: the fp8 and sequence-segment variants; "
                          "workloads: every synthetic workload's GPU time and oracle rate")
     return ap.parse_args()
 
@@ -557,7 +558,7 @@ def main():
     if args.only in ("decode", "all"):
         dec = bench_decode(args, torch, binding, synth)
         result["decode"] = dec
-    if args.only == "all":
+    if args.only in ("variants", "all"):
         result["variants"] = bench_variants(args, torch, binding, synth)
     if train is not None and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, train)
