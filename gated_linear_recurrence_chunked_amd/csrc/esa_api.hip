@@ -128,6 +128,20 @@ int layout_of(const Problem& pr, Layout* L) {
     return ESA_OK;
 }
 
+// The block of the reproducible look-back (0 without ESA_DETERMINISTIC): the smallest power
+// of two K with K x (chains of the launch) >= kDetTilesInFlight, at most kDetMaxBlock.  A
+// chain's inclusive values then move K tiles per hop, about as fast as the workgroups in
+// flight on that chain consume tiles, while each tile's walk stays under K words.  It depends
+// on the shape only, so a shape's results are the same on every run.
+constexpr uint64_t kDetTilesInFlight = 64;
+constexpr uint32_t kDetMaxBlock = 16;
+uint32_t det_block(const Problem& pr, uint32_t nCB) {
+    if (!pr.det) return 0;
+    uint32_t k = 1;
+    while (k < kDetMaxBlock && (uint64_t)nCB * k < kDetTilesInFlight) k <<= 1;
+    return k;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Range {
@@ -282,7 +296,7 @@ int scan_bwd_impl(bool grads, int64_t B, int64_t T, int64_t H, int64_t Dh, int d
         f.nck = L.nck;
         f.nCB = L.nCB;
         f.nTiles = L.nTilesF;
-        f.det = pr.det;
+        f.det = det_block(pr, L.nCB);
         f.withhold = 0;  // the checkpoint pass never takes the test instance
         rc = set_epoch(s, hdr, &f.epoch, &f.epochWord);
         if (rc != ESA_OK) return rc;
@@ -311,7 +325,7 @@ int scan_bwd_impl(bool grads, int64_t B, int64_t T, int64_t H, int64_t Dh, int d
     p.nck = L.nck;
     p.nCB = L.nCB;
     p.nTiles = L.nTilesB;
-    p.det = pr.det;
+    p.det = det_block(pr, L.nCB);
     p.withhold = pr.forceTimeout;
     rc = set_epoch(s, hdr, &p.epoch, &p.epochWord);
     if (rc != ESA_OK) return rc;
@@ -406,7 +420,7 @@ int esa_scan_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mod
     p.nck = L.nck;
     p.nCB = L.nCB;
     p.nTiles = L.nTilesF;
-    p.det = pr.det;
+    p.det = det_block(pr, L.nCB);
     p.withhold = pr.forceTimeout;
     rc = set_epoch(s, p.hdr, &p.epoch, &p.epochWord);
     if (rc != ESA_OK) return rc;
@@ -493,7 +507,7 @@ int esa_scan_segment_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype,
     f.nck = L.nck;
     f.nCB = L.nCB;
     f.nTiles = L.nTilesF;
-    f.det = pr.det;
+    f.det = det_block(pr, L.nCB);
     f.withhold = 0;
     rc = set_epoch(s, f.hdr, &f.epoch, &f.epochWord);
     if (rc != ESA_OK) return rc;

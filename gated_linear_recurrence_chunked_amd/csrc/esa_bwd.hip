@@ -212,17 +212,18 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         float carry = 0.0f;
         if (FULL || gl < p.nLanes) {
             uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
+            const bool inc = det_publishes_inc(p.nTiles - 1 - tile, p.det);
             if (tile == p.nTiles - 1) {
                 carry = p.dET ? p.dET[gl] : 0.0f;
             } else {
                 float pin;  // unused: the backward carries no gate product
                 carry = chain_carry<false, TEST ? kTestSpinLimit : kSpinLimit>(
                     p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc, p.hdr, tp, te, &pin,
-                    p.det != 0);
+                    p.det, inc);
             }
             const float lam_out = te + tp * carry;
-            if (!TEST || tile != p.nTiles - 1)  // the test instance withholds the last tile
-                publish(X, tagInc, lam_out);
+            // the test instance withholds the last tile
+            if ((!TEST || tile != p.nTiles - 1) && inc) publish(X, tagInc, lam_out);
             if (tile == 0 && p.de0) p.de0[gl] = lam_out;
         }
         sCarry[ch] = carry;

@@ -172,7 +172,7 @@ struct FwdParams {
     uint32_t nTiles;
     uint32_t epoch;  // tags of this call's look-back words (host epoch)
     const uint32_t* epochWord;  // non-NULL: read the epoch here instead (graph-recorded launch)
-    uint32_t det;    // non-zero: every tile waits for its neighbour's inclusive value
+    uint32_t det;    // 0, or the block of the reproducible look-back (a power of two)
     uint32_t withhold;  // non-zero: launch the forced-timeout test instance (see launch_fwd)
 };
 
@@ -603,26 +603,24 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
     int64_t j = tile + step;
     uint32_t polls = 0;
     for (;;) {
+        // both words of the slot in one round trip
         const uint64_t x = peek(flagX + j * nLanes + lane);
+        const uint64_t yv = peek(flagY + j * nLanes + lane);
         const uint32_t tg = word_tag(x);
         if (tg == tagInc) {
             if constexpr (!PROD) return ae + ap * word_val(x);
             // the inclusive product is published beside the inclusive state, in no fixed
             // order: wait until it is visible too
-            const uint64_t yv = peek(flagY + j * nLanes + lane);
             if (word_tag(yv) == tagInc) {
                 *pinc = ap * word_val(yv);
                 return ae + ap * word_val(x);
             }
         }
-        if (tg == tagAgg) {
-            const uint64_t yv = peek(flagY + j * nLanes + lane);
-            if (word_tag(yv) == tagAgg) {
-                ae = ae + ap * word_val(x);
-                ap = ap * word_val(yv);
-                j += step;
-                continue;
-            }
+        if (tg == tagAgg && word_tag(yv) == tagAgg) {
+            ae = ae + ap * word_val(x);
+            ap = ap * word_val(yv);
+            j += step;
+            continue;
         }
         if (!wait_turn<LIMIT>(++polls, hdr)) {
             if constexpr (PROD) *pinc = __builtin_nanf("");
@@ -640,47 +638,42 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
 // Successors cope with a tile that never publishes an aggregate: they wait for its
 // inclusive word, which follows without any wait of its own.
 //
-// With `det` the tile always waits for its neighbour's inclusive value: every carry is then
-// the same fp32 expression on every run (bitwise reproducible results), at the price of
-// resolving a chain's tiles one after another (free when a chain has about one tile
-// resident at a time, as at 64K context; ~10x slower for a single long chain).
+// With `det` = K (a power of two) the chain is cut into blocks of K tiles, counted from its
+// start, and only the chain's first tile and the last tile of each block publish inclusive
+// values; the others publish their aggregate pair and nothing else (det_publishes_inc).
+// Every word slot then only ever holds one kind of word, so the walk below folds exactly the
+// aggregates back to the nearest publisher and ends at its inclusive value: the carry is the
+// same fp32 expression on every run (bitwise reproducible results), whatever the timing.  K
+// = 1 waits for the neighbour's inclusive value.  The host picks K from the number of chains
+// so that a block's walk stays short while the inclusive values still move K tiles per hop.
 template <bool PROD = false, uint32_t LIMIT = kSpinLimit>
 __device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, int64_t nLanes,
                                              int64_t lane, int64_t tile, int step, uint32_t tagAgg,
                                              uint32_t tagInc, uint32_t* hdr, float tp, float te,
-                                             float* pin, bool det) {
-    const int64_t nb = (tile + step) * nLanes + lane;
-    if (det) {
-        uint32_t polls = 0;
-        for (;;) {
-            const uint64_t x = peek(flagX + nb);
-            if (word_tag(x) == tagInc) {
-                if constexpr (!PROD) return word_val(x);
-                const uint64_t y = peek(flagY + nb);
-                if (word_tag(y) == tagInc) {
-                    *pin = word_val(y);
-                    return word_val(x);
-                }
-            }
-            if (!wait_turn<LIMIT>(++polls, hdr)) {
-                if constexpr (PROD) *pin = __builtin_nanf("");
-                return __builtin_nanf("");
+                                             float* pin, uint32_t det, bool pubInc) {
+    if (det == 0u) {
+        const uint64_t x = peek(flagX + (tile + step) * nLanes + lane);
+        if (word_tag(x) == tagInc) {
+            if constexpr (!PROD) return word_val(x);
+            const uint64_t y = peek(flagY + (tile + step) * nLanes + lane);
+            if (word_tag(y) == tagInc) {
+                *pin = word_val(y);
+                return word_val(x);
             }
         }
     }
-    const uint64_t x = peek(flagX + nb);
-    if (word_tag(x) == tagInc) {
-        if constexpr (!PROD) return word_val(x);
-        const uint64_t y = peek(flagY + nb);
-        if (word_tag(y) == tagInc) {
-            *pin = word_val(y);
-            return word_val(x);
-        }
+    if (det == 0u || !pubInc) {
+        publish(flagX + tile * nLanes + lane, tagAgg, te);
+        publish(flagY + tile * nLanes + lane, tagAgg, tp);
     }
-    publish(flagX + tile * nLanes + lane, tagAgg, te);
-    publish(flagY + tile * nLanes + lane, tagAgg, tp);
     return look_back<PROD, LIMIT>(flagX, flagY, nLanes, lane, tile, step, tagAgg, tagInc, hdr,
                                   pin);
+}
+
+// Whether the tile at position `pos` along its chain (0 = the chain's first tile) publishes
+// its inclusive value under `det` (see chain_carry).
+__device__ __forceinline__ bool det_publishes_inc(uint32_t pos, uint32_t det) {
+    return det == 0u || pos == 0u || (pos & (det - 1u)) == det - 1u;
 }
 
 // Workgroup -> (tile row, channel block).  Workgroup i runs on XCD i mod 8.  When the channel

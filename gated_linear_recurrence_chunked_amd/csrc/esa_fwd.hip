@@ -118,14 +118,16 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
             uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
             uint64_t* Y = p.flagY + (int64_t)tile * p.nLanes + gl;
             float pin = 1.0f;  // PROD: product of the gates of every earlier tile
+            const bool inc = det_publishes_inc(tile, p.det);
             if (tile == 0) {
                 carry = p.e0 ? p.e0[gl] : 0.0f;
             } else {
                 carry = chain_carry<PROD, TEST ? kTestSpinLimit : kSpinLimit>(
                     p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg, tagInc, p.hdr, tp, te, &pin,
-                    p.det != 0);
+                    p.det, inc);
             }
-            const bool pub = !TEST || tile != 0;  // the test instance withholds tile 0
+            // the test instance withholds tile 0
+            const bool pub = (!TEST || tile != 0) && inc;
             if constexpr (PROD) {
                 if (pub) publish(Y, tagInc, tp * pin);
                 if (tile == p.nTiles - 1) p.prod[gl] = tp * pin;

@@ -107,15 +107,29 @@ def test_repeated_runs_agree():
     check_abort_clear()
 
 
-@pytest.mark.parametrize("dt,mode", [(torch.float16, "controlled"), (torch.float32, "direct")])
-def test_deterministic_flag_gives_bitwise_identical_runs(dt, mode):
+# (storage, form, B, T, H, Dh, gate mean): the chains of a launch (B*H*Dh over the channel
+# block: 64 channels, 128 for fp8) pick the block K of the reproducible look-back (16 up to
+# 4 chains, then 8, 4, 2, 1 at 8, 16, 32, 64 chains).
+DET_CASES = [
+    (torch.float16, "controlled", 1, 20000, 2, 64, 1.0),   # 2 chains, K = 16
+    (torch.float32, "direct", 1, 20000, 2, 64, 1.0),       # 2 chains, K = 16
+    (torch.float8_e4m3fn, "controlled", 1, 20000, 2, 64, 1.0),  # 1 chain, K = 16
+    (torch.float16, "controlled", 2, 5000, 8, 64, 4.0),    # 16 chains, K = 4, long memory
+    (torch.bfloat16, "direct", 4, 3001, 8, 64, 3.0),       # 32 chains, K = 2
+    (torch.float16, "controlled", 8, 1500, 8, 64, 1.0),    # 64 chains, K = 1
+]
+
+
+@pytest.mark.parametrize("dt,mode,B,T,H,Dh,mu", DET_CASES,
+                         ids=[f"{str(c[0])[6:]}-{c[1]}-B{c[2]}T{c[3]}H{c[4]}" for c in DET_CASES])
+def test_deterministic_flag_gives_bitwise_identical_runs(dt, mode, B, T, H, Dh, mu):
     """ESA_DETERMINISTIC: every run of the forward, the backward and the segment pass gives
-    the same bits, on a shape whose two chains have many tiles in flight at once (where the
-    default look-back combines whatever is published and may differ in the last bits)."""
-    B, T, H, Dh = 1, 20000, 2, 64
-    say(f"deterministic {dt} {mode}")
+    the same bits, on shapes whose chains have many tiles in flight at once (where the
+    default look-back combines whatever is published and may differ in the last bits), one
+    for each size of the position-fixed block of tiles, ragged tails included."""
+    say(f"deterministic {dt} {mode} B={B} T={T} H={H} Dh={Dh}")
     shp = (B, T, H, Dh)
-    x = {k: synth.normal(shp, 920 + i, 1.0 if k == "a" else 0.0, 1.5 if k == "a" else 1.0, dt)
+    x = {k: synth.normal(shp, 920 + i, mu if k == "a" else 0.0, 1.5 if k == "a" else 1.0, dt)
          for i, k in enumerate(("a", "v", "q", "dy"))}
     e0 = synth.random_state(B, H, Dh, 925)
     g = {k: t.to(DEV) for k, t in x.items()}
@@ -130,9 +144,11 @@ def test_deterministic_flag_gives_bitwise_identical_runs(dt, mode):
         runs.append((y, eT, ck) + tuple(grads) + tuple(seg))
     torch.cuda.synchronize()
     check_abort_clear()
+    bits = {torch.float32: torch.int32, torch.float16: torch.int16, torch.bfloat16: torch.int16,
+            torch.float8_e4m3fn: torch.uint8, torch.float8_e5m2: torch.uint8}
     for r in runs[1:]:
         for got, ref in zip(r, runs[0]):
-            assert torch.equal(got, ref)
+            assert torch.equal(got.view(bits[got.dtype]), ref.view(bits[ref.dtype]))
     m = 0 if mode == "direct" else 1
     ry, reT = oracle.scan_fwd(x["a"], x["v"], x["q"], e0, mode=m)
     rda, rdv, rdq, rde0 = oracle.scan_bwd(x["a"], x["v"], x["q"], x["dy"], e0, None, mode=m)
