@@ -23,7 +23,7 @@
 
 namespace esa {
 
-template <typename T, int MODE, int DH, int L, int NT, bool GRADS, bool FULL, bool TEST>
+template <typename T, int MODE, int DH, int L, int NT, bool GRADS, bool FULL, int CHAIN>
 __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint32_t cb, float* sP,
                                          float* sE, float* sWP, float* sWE, float* sCarry) {
     using G = Geom<T, DH, L, NT>;
@@ -212,14 +212,16 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         float carry = 0.0f;
         if (FULL || gl < p.nLanes) {
             uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
-            const bool inc = det_publishes_inc(p.nTiles - 1 - tile, p.det);
+            constexpr bool TEST = CHAIN == kChainTest;
+            const uint32_t det = CHAIN == kChainDefault ? 0u : p.det;
+            const bool inc = det_publishes_inc(p.nTiles - 1 - tile, det);
             if (tile == p.nTiles - 1) {
                 carry = p.dET ? p.dET[gl] : 0.0f;
             } else {
                 float pin;  // unused: the backward carries no gate product
                 carry = chain_carry<false, TEST ? kTestSpinLimit : kSpinLimit>(
                     p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc, p.hdr, tp, te, &pin,
-                    p.det, inc);
+                    det, inc);
             }
             const float lam_out = te + tp * carry;
             // the test instance withholds the last tile
@@ -258,7 +260,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     }
 }
 
-template <typename T, int MODE, int DH, int L, int NT, bool GRADS, bool TEST = false>
+template <typename T, int MODE, int DH, int L, int NT, bool GRADS, int CHAIN>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     using G = Geom<T, DH, L, NT>;
     constexpr int CB = G::CB, TT = G::TT, NW = G::NW;
@@ -276,27 +278,39 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     const bool full = (int64_t)(tile + 1) * TT <= p.T && (int64_t)(cb + 1) * CB <= p.nLanes &&
                       p.C % CB == 0 && (int64_t)TT * p.C * (int64_t)sizeof(T) < (int64_t(1) << 31);
     if (full)
-        bwd_tile<T, MODE, DH, L, NT, GRADS, true, TEST>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
+        bwd_tile<T, MODE, DH, L, NT, GRADS, true, CHAIN>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
     else
-        bwd_tile<T, MODE, DH, L, NT, GRADS, false, TEST>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
+        bwd_tile<T, MODE, DH, L, NT, GRADS, false, CHAIN>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
+}
+
+template <typename T, int MODE, int DH, int CHAIN>
+hipError_t launch_bwd_as(const BwdParams& p, hipStream_t s) {
+    using C = BwdCfg<T, DH>;
+    const dim3 grid(p.nCB * p.nTiles), block(C::NT);
+    if (p.da)
+        hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT, true, CHAIN>), grid, block, 0, s,
+                           p);
+    else
+        hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT, false, CHAIN>), grid, block, 0, s,
+                           p);
+    return hipGetLastError();
 }
 
 template <typename T, int MODE, int DH>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
-    using C = BwdCfg<T, DH>;
-    const dim3 grid(p.nCB * p.nTiles), block(C::NT);
     if (p.da && p.withhold) {
         // the forced-timeout test instance: fp16 storage and Dh = 64 only (as the forward)
-        if constexpr (std::is_same<T, _Float16>::value && DH == 64)
-            hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT, true, true>), grid, block, 0, s,
-                               p);
-        else
+        if constexpr (std::is_same<T, _Float16>::value && DH == 64) {
+            using C = BwdCfg<T, DH>;
+            hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT, true, kChainTest>),
+                               dim3(p.nCB * p.nTiles), dim3(C::NT), 0, s, p);
+            return hipGetLastError();
+        } else {
             return hipErrorNotSupported;
-    } else if (p.da)
-        hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT, true>), grid, block, 0, s, p);
-    else
-        hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT, false>), grid, block, 0, s, p);
-    return hipGetLastError();
+        }
+    }
+    return p.det ? launch_bwd_as<T, MODE, DH, kChainDet>(p, s)
+                 : launch_bwd_as<T, MODE, DH, kChainDefault>(p, s);
 }
 
 #define ESA_INST_BWD(T, M, D) template hipError_t launch_bwd<T, M, D>(const BwdParams&, hipStream_t);

@@ -646,6 +646,12 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
 // same fp32 expression on every run (bitwise reproducible results), whatever the timing.  K
 // = 1 waits for the neighbour's inclusive value.  The host picks K from the number of chains
 // so that a block's walk stays short while the inclusive values still move K tiles per hop.
+// Look-back variants, one kernel instance each, so the default kernels carry no code of the
+// others: the default look-back; the reproducible one (ESA_DETERMINISTIC); the forced-timeout
+// test instance (either look-back, chosen at run time, with the chain's first tile withholding
+// its publications and every wait giving up after kTestSpinLimit polls).
+enum : int { kChainDefault = 0, kChainDet = 1, kChainTest = 2 };
+
 template <bool PROD = false, uint32_t LIMIT = kSpinLimit>
 __device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, int64_t nLanes,
                                              int64_t lane, int64_t tile, int step, uint32_t tagAgg,

@@ -17,7 +17,7 @@
 namespace esa {
 
 template <typename T, int MODE, int DH, int L, int NT, bool READOUT, bool PROD, bool FULL,
-          bool TEST>
+          int CHAIN>
 __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint32_t cb,
                                          float* sP, float* sE, float* sWP, float* sWE,
                                          float* sCarry) {
@@ -118,13 +118,15 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
             uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
             uint64_t* Y = p.flagY + (int64_t)tile * p.nLanes + gl;
             float pin = 1.0f;  // PROD: product of the gates of every earlier tile
-            const bool inc = det_publishes_inc(tile, p.det);
+            constexpr bool TEST = CHAIN == kChainTest;
+            const uint32_t det = CHAIN == kChainDefault ? 0u : p.det;
+            const bool inc = det_publishes_inc(tile, det);
             if (tile == 0) {
                 carry = p.e0 ? p.e0[gl] : 0.0f;
             } else {
                 carry = chain_carry<PROD, TEST ? kTestSpinLimit : kSpinLimit>(
                     p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg, tagInc, p.hdr, tp, te, &pin,
-                    p.det, inc);
+                    det, inc);
             }
             // the test instance withholds tile 0
             const bool pub = (!TEST || tile != 0) && inc;
@@ -211,7 +213,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
     }
 }
 
-template <typename T, int MODE, int DH, int L, int NT, bool READOUT, bool PROD, bool TEST = false>
+template <typename T, int MODE, int DH, int L, int NT, bool READOUT, bool PROD, int CHAIN>
 __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     static_assert(!(READOUT && PROD), "the gate product comes from the state-only pass");
     using G = Geom<T, DH, L, NT>;
@@ -229,32 +231,45 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     const bool full = (int64_t)(tile + 1) * TT <= p.T && (int64_t)(cb + 1) * CB <= p.nLanes &&
                       p.C % CB == 0 && (int64_t)TT * p.C * (int64_t)sizeof(T) < (int64_t(1) << 31);
     if (full)
-        fwd_tile<T, MODE, DH, L, NT, READOUT, PROD, true, TEST>(p, tile, cb, sP, sE, sWP, sWE,
+        fwd_tile<T, MODE, DH, L, NT, READOUT, PROD, true, CHAIN>(p, tile, cb, sP, sE, sWP, sWE,
                                                                  sCarry);
     else
-        fwd_tile<T, MODE, DH, L, NT, READOUT, PROD, false, TEST>(p, tile, cb, sP, sE, sWP, sWE,
+        fwd_tile<T, MODE, DH, L, NT, READOUT, PROD, false, CHAIN>(p, tile, cb, sP, sE, sWP, sWE,
                                                                   sCarry);
+}
+
+template <typename T, int MODE, int DH, int CHAIN>
+hipError_t launch_fwd_as(const FwdParams& p, hipStream_t s) {
+    using C = FwdCfg<T, DH>;
+    const dim3 grid(p.nCB * p.nTiles), block(C::NT);
+    if (p.y)
+        hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, true, false, CHAIN>), grid, block,
+                           0, s, p);
+    else if (p.prod)
+        hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, false, true, CHAIN>), grid, block,
+                           0, s, p);
+    else
+        hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, false, false, CHAIN>), grid, block,
+                           0, s, p);
+    return hipGetLastError();
 }
 
 template <typename T, int MODE, int DH>
 hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
-    using C = FwdCfg<T, DH>;
-    const dim3 grid(p.nCB * p.nTiles), block(C::NT);
     if (p.y && p.withhold) {
         // the forced-timeout test instance exists for fp16 storage and Dh = 64 only (the host
         // rejects the flag for other problems)
-        if constexpr (std::is_same<T, _Float16>::value && DH == 64)
-            hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, true, false, true>), grid, block,
-                               0, s, p);
-        else
+        if constexpr (std::is_same<T, _Float16>::value && DH == 64) {
+            using C = FwdCfg<T, DH>;
+            hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, true, false, kChainTest>),
+                               dim3(p.nCB * p.nTiles), dim3(C::NT), 0, s, p);
+            return hipGetLastError();
+        } else {
             return hipErrorNotSupported;
-    } else if (p.y)
-        hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, true, false>), grid, block, 0, s, p);
-    else if (p.prod)
-        hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, false, true>), grid, block, 0, s, p);
-    else
-        hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, false, false>), grid, block, 0, s, p);
-    return hipGetLastError();
+        }
+    }
+    return p.det ? launch_fwd_as<T, MODE, DH, kChainDet>(p, s)
+                 : launch_fwd_as<T, MODE, DH, kChainDefault>(p, s);
 }
 
 #define ESA_INST_FWD(T, M, D) template hipError_t launch_fwd<T, M, D>(const FwdParams&, hipStream_t);
