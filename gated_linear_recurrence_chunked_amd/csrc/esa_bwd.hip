@@ -30,6 +30,8 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, HL = G::HL;
     constexpr int TT = G::TT;
     constexpr int ES = sizeof(T);
+    constexpr bool CQ = sizeof(T) == 4;  // fp32 storage carries gate products as complements
+    using Q = GP<CQ>;
     const uint32_t epoch = launch_epoch(p.epoch, p.epochWord);
     const uint32_t tagAgg = make_tag(epoch, kTagAgg);
     const uint32_t tagInc = make_tag(epoch, kTagInc);
@@ -100,12 +102,13 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     }
 
     // ---- gates and the thread's forward fold ----
-    // S_[i][e] = s; U_[i][e] = 1 - s (controlled) or s (1 - s) (direct); V_[i][e] = v
+    // S_[i][e] = s (or 1 - s with complements); U_[i][e] = 1 - s (controlled, products) or
+    // s (1 - s); V_[i][e] = v
     float S_[L][VEC], U_[L][VEC], V_[L][VEC];
     float P[VEC], E[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-        P[e] = 1.0f;
+        P[e] = Q::one;
         E[e] = 0.0f;
     }
 #pragma unroll
@@ -120,11 +123,11 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
             gate<T>(av[e], s, u);
             s = ok ? s : 1.0f;
             u = ok ? u : 0.0f;
-            S_[i][e] = s;
-            U_[i][e] = MODE == kDirect ? s * u : u;
+            S_[i][e] = CQ ? u : s;
+            U_[i][e] = MODE == kDirect || CQ ? s * u : u;
             const float bt = MODE == kDirect ? (ok ? V_[i][e] : 0.0f) : u * V_[i][e];
-            E[e] = s * E[e] + bt;
-            P[e] = P[e] * s;
+            E[e] = Q::apply(S_[i][e], E[e]) + bt;
+            P[e] = Q::mul(P[e], S_[i][e]);
         }
     }
 
@@ -133,13 +136,13 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     const int w = tid / kWave;
     float xp[G::CPL][G::SPW], xe[G::CPL][G::SPW];
     float XP[VEC], XE[VEC];
-    slots_phase_a<G, false>(P, E, sP, sE, sWP, sWE, xp, xe);
+    slots_phase_a<G, false, CQ>(P, E, sP, sE, sWP, sWE, xp, xe);
     __syncthreads();
-    slots_phase_b<G, false>(sP, sE, sWP, sWE, xp, xe);
+    slots_phase_b<G, false, CQ>(sP, sE, sWP, sWE, xp, xe);
     __syncthreads();
     read_exclusive<G>(sP, sE, XP, XE);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) E[e] = XE[e] + XP[e] * cin[e];
+    for (int e = 0; e < VEC; ++e) E[e] = XE[e] + Q::apply(XP[e], cin[e]);
 
     // ---- re-run the forward per step; readout backward; keep gE and the gate factor ----
     float Gr[L][VEC];
@@ -151,8 +154,9 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             Eprev[e] = E[e];
-            const float bt = MODE == kDirect ? (ok ? V_[i][e] : 0.0f) : U_[i][e] * V_[i][e];
-            E[e] = S_[i][e] * E[e] + bt;
+            const float uc = CQ ? S_[i][e] : U_[i][e];  // 1 - s
+            const float bt = MODE == kDirect ? (ok ? V_[i][e] : 0.0f) : uc * V_[i][e];
+            E[e] = Q::apply(S_[i][e], E[e]) + bt;
             ss += E[e] * E[e];
         }
         ss = head_sum<HL>(ss);
@@ -174,7 +178,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         for (int e = 0; e < VEC; ++e) {
             Gr[i][e] = ok ? r * (dn[e] - n[e] * mu) : 0.0f;
             // gate factor w, stored over V_: d_logit = dE * w
-            const float su = MODE == kDirect ? U_[i][e] : S_[i][e] * U_[i][e];
+            const float su = MODE == kDirect || CQ ? U_[i][e] : S_[i][e] * U_[i][e];
             V_[i][e] = MODE == kDirect ? Eprev[e] * su : (Eprev[e] - V_[i][e]) * su;
         }
         if constexpr (GRADS) {
@@ -188,26 +192,26 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     // ---- reverse fold of the thread's steps: lam_out = P * lam_in + E ----
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-        float pr = 1.0f, er = 0.0f;
+        float pr = Q::one, er = 0.0f;
 #pragma unroll
         for (int i = L - 1; i >= 0; --i) {
-            er = S_[i][e] * (Gr[i][e] + er);
-            pr = S_[i][e] * pr;
+            er = Q::apply(S_[i][e], Gr[i][e] + er);
+            pr = Q::mul(S_[i][e], pr);
         }
         P[e] = pr;
         E[e] = er;
     }
     // the slot arrays are reused: this thread's slot positions were last read by this thread,
     // and the wave aggregates by every wave before the barrier above
-    slots_phase_a<G, true>(P, E, sP, sE, sWP, sWE, xp, xe);
+    slots_phase_a<G, true, CQ>(P, E, sP, sE, sWP, sWE, xp, xe);
     __syncthreads();
-    slots_phase_b<G, true>(sP, sE, sWP, sWE, xp, xe);
+    slots_phase_b<G, true, CQ>(sP, sE, sWP, sWE, xp, xe);
 
     // ---- reverse look-back across tiles, wave k for channels 64k.. (lane = channel) ----
     if (w < G::CPL) {
         const int ch = (tid % kWave) + w * kWave;
         float tp, te;
-        tile_total<G, true>(sWP, sWE, ch, tp, te);
+        tile_total<G, true, CQ>(sWP, sWE, ch, tp, te);
         const int64_t gl = (int64_t)cb * CB + ch;
         float carry = 0.0f;
         if (FULL || gl < p.nLanes) {
@@ -219,11 +223,11 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
                 carry = p.dET ? p.dET[gl] : 0.0f;
             } else {
                 float pin;  // unused: the backward carries no gate product
-                carry = chain_carry<false, TEST ? kTestSpinLimit : kSpinLimit>(
+                carry = chain_carry<false, TEST ? kTestSpinLimit : kSpinLimit, CQ>(
                     p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc, p.hdr, tp, te, &pin,
                     det, inc);
             }
-            const float lam_out = te + tp * carry;
+            const float lam_out = te + Q::apply(tp, carry);
             // the test instance withholds the last tile
             if ((!TEST || tile != p.nTiles - 1) && inc) publish(X, tagInc, lam_out);
             if (tile == 0 && p.de0) p.de0[gl] = lam_out;
@@ -236,7 +240,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     // ---- reverse recurrence over the thread's steps; gate and value gradients ----
     float lam[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) lam[e] = XE[e] + XP[e] * sCarry[j * VEC + e];
+    for (int e = 0; e < VEC; ++e) lam[e] = XE[e] + Q::apply(XP[e], sCarry[j * VEC + e]);
 #pragma unroll
     for (int i = L - 1; i >= 0; --i) {
         const bool ok = FULL || (lane_ok && t0 + i < p.T);
@@ -244,9 +248,9 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const float dE = Gr[i][e] + lam[e];
-            lam[e] = S_[i][e] * dE;
+            lam[e] = Q::apply(S_[i][e], dE);
             dav[e] = dE * V_[i][e];
-            dvv[e] = MODE == kDirect ? dE : dE * U_[i][e];
+            dvv[e] = MODE == kDirect ? dE : dE * (CQ ? S_[i][e] : U_[i][e]);
         }
         if constexpr (GRADS) {
             if constexpr (FULL) {

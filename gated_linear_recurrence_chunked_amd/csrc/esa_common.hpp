@@ -445,7 +445,32 @@ __device__ __forceinline__ float head_sum(float x) {
 // Forward pairs compose earlier first, (P1, E1) o (P2, E2) = (P1 P2, E2 + P2 E1); reverse
 // maps lam_out = P lam_in + E compose the later side first; both reduce to the same update
 // (te, tp) <- (p te + e, tp p) in their own walking order.
-template <class G, bool REV>
+// Gate products of a pair, in one of two representations.  GP<false> carries the product P
+// itself.  GP<true> carries its complement q = 1 - P, for fp32 storage: there the gates of a
+// retentive lane lie within 1e-4 of 1, and the fp32 product of two such factors drops its
+// second-order term (below half a unit in the last place next to 1), always in the same
+// direction; the cross-tile carry c <- e + P c divides that bias by 1 - P, so the state drifts
+// along the sequence.  The complement of a product, q1 + q2 - q1 q2, keeps its relative
+// precision, and (1 - q) x = x - q x loses nothing next to 1.  Where P is small instead, the
+// complement leaves an absolute error of about one unit in the last place of x in (1 - q) x,
+// i.e. relative to the state being decayed, which the parity metric's scale already covers.
+// The 16-bit and 8-bit storages keep GP<false>: their bars are 500x wider than that drift.
+template <bool CQ>
+struct GP;
+template <>
+struct GP<false> {
+    static constexpr float one = 1.0f;
+    __device__ static __forceinline__ float mul(float a, float b) { return a * b; }
+    __device__ static __forceinline__ float apply(float p, float x) { return p * x; }
+};
+template <>
+struct GP<true> {
+    static constexpr float one = 0.0f;
+    __device__ static __forceinline__ float mul(float a, float b) { return __builtin_fmaf(-a, b, a) + b; }
+    __device__ static __forceinline__ float apply(float q, float x) { return __builtin_fmaf(-q, x, x); }
+};
+
+template <class G, bool REV, bool CQ = false>
 __device__ __forceinline__ void slots_phase_a(const float* P, const float* E, float* sP, float* sE,
                                               float* sWP, float* sWE,
                                               float (&xp)[G::CPL][G::SPW],
@@ -465,7 +490,7 @@ __device__ __forceinline__ void slots_phase_a(const float* P, const float* E, fl
 #pragma unroll
     for (int k = 0; k < G::CPL; ++k) {
         const int ch = lane + k * kWave;
-        float tp = 1.0f, te = 0.0f;
+        float tp = GP<CQ>::one, te = 0.0f;
 #pragma unroll
         for (int q = 0; q < SPW; ++q) {
             const int sw = REV ? SPW - 1 - q : q;
@@ -473,15 +498,15 @@ __device__ __forceinline__ void slots_phase_a(const float* P, const float* E, fl
             const float ps = sP[s * CB + ch], es = sE[s * CB + ch];
             xp[k][sw] = tp;
             xe[k][sw] = te;
-            te = ps * te + es;
-            tp = tp * ps;
+            te = GP<CQ>::apply(ps, te) + es;
+            tp = GP<CQ>::mul(tp, ps);
         }
         sWP[w * CB + ch] = tp;
         sWE[w * CB + ch] = te;
     }
 }
 
-template <class G, bool REV>
+template <class G, bool REV, bool CQ = false>
 __device__ __forceinline__ void slots_phase_b(float* sP, float* sE, const float* sWP,
                                               const float* sWE, const float (&xp)[G::CPL][G::SPW],
                                               const float (&xe)[G::CPL][G::SPW]) {
@@ -490,37 +515,37 @@ __device__ __forceinline__ void slots_phase_b(float* sP, float* sE, const float*
 #pragma unroll
     for (int k = 0; k < G::CPL; ++k) {
         const int ch = lane + k * kWave;
-        float wp = 1.0f, we = 0.0f;  // the other waves on this slot's earlier side
+        float wp = GP<CQ>::one, we = 0.0f;  // the other waves on this slot's earlier side
 #pragma unroll
         for (int q = 0; q < NW; ++q) {
             const int v = REV ? NW - 1 - q : q;
             if (REV ? v > w : v < w) {
                 const float pv = sWP[v * CB + ch], ev = sWE[v * CB + ch];
-                we = pv * we + ev;
-                wp = wp * pv;
+                we = GP<CQ>::apply(pv, we) + ev;
+                wp = GP<CQ>::mul(wp, pv);
             }
         }
 #pragma unroll
         for (int sw = 0; sw < SPW; ++sw) {
             const int s = w * SPW + sw;
-            sP[s * CB + ch] = xp[k][sw] * wp;
-            sE[s * CB + ch] = xe[k][sw] + xp[k][sw] * we;
+            sP[s * CB + ch] = GP<CQ>::mul(xp[k][sw], wp);
+            sE[s * CB + ch] = xe[k][sw] + GP<CQ>::apply(xp[k][sw], we);
         }
     }
 }
 
 // Composition of all waves' aggregates for channel ch: the tile's own pair / map.
-template <class G, bool REV>
+template <class G, bool REV, bool CQ = false>
 __device__ __forceinline__ void tile_total(const float* sWP, const float* sWE, int ch, float& tp,
                                            float& te) {
-    tp = 1.0f;
+    tp = GP<CQ>::one;
     te = 0.0f;
 #pragma unroll
     for (int q = 0; q < G::NW; ++q) {
         const int v = REV ? G::NW - 1 - q : q;
         const float pv = sWP[v * G::CB + ch], ev = sWE[v * G::CB + ch];
-        te = pv * te + ev;
-        tp = tp * pv;
+        te = GP<CQ>::apply(pv, te) + ev;
+        tp = GP<CQ>::mul(tp, pv);
     }
 }
 
@@ -594,12 +619,13 @@ __device__ __forceinline__ bool wait_turn(uint32_t polls, uint32_t* hdr) {
     return true;
 }
 
-template <bool PROD = false, uint32_t LIMIT = kSpinLimit>
+template <bool PROD = false, uint32_t LIMIT = kSpinLimit, bool CQ = false>
 __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t* flagY,
                                            int64_t nLanes, int64_t lane, int64_t tile, int step,
                                            uint32_t tagAgg, uint32_t tagInc, uint32_t* hdr,
                                            float* pinc = nullptr) {
-    float ap = 1.0f, ae = 0.0f;
+    static_assert(!(PROD && CQ), "the gate product of a segment is carried as itself");
+    float ap = GP<CQ>::one, ae = 0.0f;
     int64_t j = tile + step;
     uint32_t polls = 0;
     for (;;) {
@@ -608,7 +634,7 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
         const uint64_t yv = peek(flagY + j * nLanes + lane);
         const uint32_t tg = word_tag(x);
         if (tg == tagInc) {
-            if constexpr (!PROD) return ae + ap * word_val(x);
+            if constexpr (!PROD) return ae + GP<CQ>::apply(ap, word_val(x));
             // the inclusive product is published beside the inclusive state, in no fixed
             // order: wait until it is visible too
             if (word_tag(yv) == tagInc) {
@@ -617,8 +643,8 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
             }
         }
         if (tg == tagAgg && word_tag(yv) == tagAgg) {
-            ae = ae + ap * word_val(x);
-            ap = ap * word_val(yv);
+            ae = ae + GP<CQ>::apply(ap, word_val(x));
+            ap = GP<CQ>::mul(ap, word_val(yv));
             j += step;
             continue;
         }
@@ -652,7 +678,7 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
 // its publications and every wait giving up after kTestSpinLimit polls).
 enum : int { kChainDefault = 0, kChainDet = 1, kChainTest = 2 };
 
-template <bool PROD = false, uint32_t LIMIT = kSpinLimit>
+template <bool PROD = false, uint32_t LIMIT = kSpinLimit, bool CQ = false>
 __device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, int64_t nLanes,
                                              int64_t lane, int64_t tile, int step, uint32_t tagAgg,
                                              uint32_t tagInc, uint32_t* hdr, float tp, float te,
@@ -672,8 +698,8 @@ __device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, i
         publish(flagX + tile * nLanes + lane, tagAgg, te);
         publish(flagY + tile * nLanes + lane, tagAgg, tp);
     }
-    return look_back<PROD, LIMIT>(flagX, flagY, nLanes, lane, tile, step, tagAgg, tagInc, hdr,
-                                  pin);
+    return look_back<PROD, LIMIT, CQ>(flagX, flagY, nLanes, lane, tile, step, tagAgg, tagInc, hdr,
+                                      pin);
 }
 
 // Whether the tile at position `pos` along its chain (0 = the chain's first tile) publishes

@@ -25,6 +25,10 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
     constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, HL = G::HL;
     constexpr int TT = G::TT;
     constexpr int ES = sizeof(T);
+    // fp32 storage carries gate products as complements (GP); the segment pass's gate
+    // product output stays a product
+    constexpr bool CQ = sizeof(T) == 4 && !PROD;
+    using Q = GP<CQ>;
     static_assert(kCkptChunk % L == 0, "checkpoint steps must end a thread's slot");
     const uint32_t epoch = launch_epoch(p.epoch, p.epochWord);
     const uint32_t tagAgg = make_tag(epoch, kTagAgg);
@@ -79,7 +83,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
     float P[VEC], E[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-        P[e] = 1.0f;
+        P[e] = Q::one;
         E[e] = 0.0f;
     }
 #pragma unroll
@@ -93,25 +97,25 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
             float s, u;
             gate<T>(av[e], s, u);
             const float bt = MODE == kDirect ? vv[e] : u * vv[e];
-            A[i][e] = ok ? s : 1.0f;
+            A[i][e] = ok ? (CQ ? u : s) : Q::one;  // the gate, or its complement
             Bt[i][e] = ok ? bt : 0.0f;
-            E[e] = A[i][e] * E[e] + Bt[i][e];
-            P[e] = P[e] * A[i][e];
+            E[e] = Q::apply(A[i][e], E[e]) + Bt[i][e];
+            P[e] = Q::mul(P[e], A[i][e]);
         }
     }
 
     // ---- level 2: slot pairs through LDS (within each wave, then across the waves) ----
     const int w = tid / kWave;
     float xp[G::CPL][G::SPW], xe[G::CPL][G::SPW];
-    slots_phase_a<G, false>(P, E, sP, sE, sWP, sWE, xp, xe);
+    slots_phase_a<G, false, CQ>(P, E, sP, sE, sWP, sWE, xp, xe);
     __syncthreads();
-    slots_phase_b<G, false>(sP, sE, sWP, sWE, xp, xe);
+    slots_phase_b<G, false, CQ>(sP, sE, sWP, sWE, xp, xe);
 
     // ---- level 3: decoupled look-back across tiles, wave k for channels 64k.. (lane = channel) ----
     if (w < G::CPL) {
         const int ch = (tid % kWave) + w * kWave;
         float tp, te;
-        tile_total<G, false>(sWP, sWE, ch, tp, te);
+        tile_total<G, false, CQ>(sWP, sWE, ch, tp, te);
         const int64_t gl = (int64_t)cb * CB + ch;
         float carry = 0.0f;
         if (FULL || gl < p.nLanes) {
@@ -124,7 +128,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
             if (tile == 0) {
                 carry = p.e0 ? p.e0[gl] : 0.0f;
             } else {
-                carry = chain_carry<PROD, TEST ? kTestSpinLimit : kSpinLimit>(
+                carry = chain_carry<PROD, TEST ? kTestSpinLimit : kSpinLimit, CQ>(
                     p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg, tagInc, p.hdr, tp, te, &pin,
                     det, inc);
             }
@@ -134,7 +138,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
                 if (pub) publish(Y, tagInc, tp * pin);
                 if (tile == p.nTiles - 1) p.prod[gl] = tp * pin;
             }
-            if (pub) publish(X, tagInc, te + tp * carry);
+            if (pub) publish(X, tagInc, te + Q::apply(tp, carry));
         }
         sCarry[ch] = carry;
     }
@@ -151,7 +155,8 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         const int64_t tend = (t0 + L < p.T ? t0 + L : p.T) - 1;
         if ((FULL || lane_ok) && t0 < p.T) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) E[e] = E[e] + P[e] * (XE[e] + XP[e] * sCarry[j * VEC + e]);
+            for (int e = 0; e < VEC; ++e)
+                E[e] = E[e] + Q::apply(P[e], XE[e] + Q::apply(XP[e], sCarry[j * VEC + e]));
             if (p.ckpt && (((tend + 1) % kCkptChunk) == 0 || tend == p.T - 1)) {
                 float* dst = p.ckpt + (b * p.nck + tend / kCkptChunk) * p.C + c;
 #pragma unroll
@@ -173,7 +178,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         float XP[VEC], XE[VEC];
         read_exclusive<G>(sP, sE, XP, XE);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) E[e] = XE[e] + XP[e] * sCarry[j * VEC + e];
+        for (int e = 0; e < VEC; ++e) E[e] = XE[e] + Q::apply(XP[e], sCarry[j * VEC + e]);
     }
     const int64_t ckbase = b * p.nck;
 #pragma unroll
@@ -183,7 +188,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         float ss = 0.0f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            E[e] = A[i][e] * E[e] + Bt[i][e];
+            E[e] = Q::apply(A[i][e], E[e]) + Bt[i][e];
             ss += E[e] * E[e];
         }
         if constexpr (READOUT) {
