@@ -123,10 +123,11 @@ DET_CASES = [
 @pytest.mark.parametrize("dt,mode,B,T,H,Dh,mu", DET_CASES,
                          ids=[f"{str(c[0])[6:]}-{c[1]}-B{c[2]}T{c[3]}H{c[4]}" for c in DET_CASES])
 def test_deterministic_flag_gives_bitwise_identical_runs(dt, mode, B, T, H, Dh, mu):
-    """ESA_DETERMINISTIC: every run of the forward, the backward and the segment pass gives
-    the same bits, on shapes whose chains have many tiles in flight at once (where the
-    default look-back combines whatever is published and may differ in the last bits), one
-    for each size of the position-fixed block of tiles, ragged tails included."""
+    """ESA_DETERMINISTIC: every run of the forward, the backward (with and without a
+    checkpoint) and the segment pass gives the same bits, on shapes whose chains have many
+    tiles in flight at once (where the default look-back combines whatever is published and
+    may differ in the last bits), one for each size of the position-fixed block of tiles,
+    ragged tails included."""
     say(f"deterministic {dt} {mode} B={B} T={T} H={H} Dh={Dh}")
     shp = (B, T, H, Dh)
     x = {k: synth.normal(shp, 920 + i, mu if k == "a" else 0.0, 1.5 if k == "a" else 1.0, dt)
@@ -141,7 +142,10 @@ def test_deterministic_flag_gives_bitwise_identical_runs(dt, mode, B, T, H, Dh, 
         grads = binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], ge0, None, ckpt=ck, mode=mode,
                                  deterministic=True)
         seg = binding.segment_fwd(g["a"], g["v"], mode=mode, deterministic=True)
-        runs.append((y, eT, ck) + tuple(grads) + tuple(seg))
+        # without a checkpoint the library runs its own state-only pass first
+        nock = binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], ge0, None, ckpt=None, mode=mode,
+                                deterministic=True)
+        runs.append((y, eT, ck) + tuple(grads) + tuple(seg) + tuple(nock))
     torch.cuda.synchronize()
     check_abort_clear()
     bits = {torch.float32: torch.int32, torch.float16: torch.int16, torch.bfloat16: torch.int16,
@@ -152,11 +156,13 @@ def test_deterministic_flag_gives_bitwise_identical_runs(dt, mode, B, T, H, Dh, 
     m = 0 if mode == "direct" else 1
     ry, reT = oracle.scan_fwd(x["a"], x["v"], x["q"], e0, mode=m)
     rda, rdv, rdq, rde0 = oracle.scan_bwd(x["a"], x["v"], x["q"], x["dy"], e0, None, mode=m)
-    y, eT, _, da, dv, dq, de0, _, _ = runs[0]
+    y, eT, _, da, dv, dq, de0, _, _, da2, dv2, dq2, de02 = runs[0]
     assert_close("y", y, ry, dt)
     assert_close("eT", eT, reT, dt)
     for name, got, ref in (("d_logit", da, rda), ("d_value", dv, rdv), ("d_query", dq, rdq),
-                           ("d_init", de0, rde0)):
+                           ("d_init", de0, rde0), ("d_logit (no ckpt)", da2, rda),
+                           ("d_value (no ckpt)", dv2, rdv), ("d_query (no ckpt)", dq2, rdq),
+                           ("d_init (no ckpt)", de02, rde0)):
         assert_close(name, got, ref, dt)
 
 
