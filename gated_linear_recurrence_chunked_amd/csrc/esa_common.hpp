@@ -19,7 +19,10 @@
 //            whose neighbour already shows an inclusive value takes it; otherwise it
 //            publishes its aggregate pair and walks back over earlier tiles' published
 //            pairs until it meets an inclusive value.  Either way it then publishes its
-//            own inclusive value.
+//            own inclusive value.  For bitwise reproducible results only fixed positions
+//            of the chain publish inclusive values (see chain_carry), so every carry folds
+//            the same pairs on every run.
+//   fp32     storage carries every gate product as its complement 1 - P (see GP).
 //
 // Tile order.  Workgroup IDs are tile-major within each XCD (see tile_of; the backward numbers
 // tiles from the end), so a tile only ever waits on tiles with smaller IDs.  The hardware
@@ -432,19 +435,6 @@ __device__ __forceinline__ float head_sum(float x) {
     return x;
 }
 
-// Exclusive scan of the per-thread pairs over the S time slots of a tile, per channel, in
-// two phases through LDS (thread = slot * NCL + channel lane, VEC channels each; the slots
-// of wave w are w*SPW .. w*SPW+SPW-1).
-//
-// Phase A: every thread stores its pair; lane = channel of each wave then walks that wave's
-// SPW slots in order (backwards for the reverse scan), keeps each slot's exclusive pair within
-// the wave in registers, and stores the wave's aggregate.  No barrier is needed inside phase
-// A: a wave only reads what it has just written, and LDS serves one wave's requests in order.
-// Phase B (after a barrier): lane = channel composes the other waves' aggregates into the
-// wave prefix and stores each slot's exclusive pair for the whole tile.
-// Forward pairs compose earlier first, (P1, E1) o (P2, E2) = (P1 P2, E2 + P2 E1); reverse
-// maps lam_out = P lam_in + E compose the later side first; both reduce to the same update
-// (te, tp) <- (p te + e, tp p) in their own walking order.
 // Gate products of a pair, in one of two representations.  GP<false> carries the product P
 // itself.  GP<true> carries its complement q = 1 - P, for fp32 storage: there the gates of a
 // retentive lane lie within 1e-4 of 1, and the fp32 product of two such factors drops its
@@ -470,6 +460,20 @@ struct GP<true> {
     __device__ static __forceinline__ float apply(float q, float x) { return __builtin_fmaf(-q, x, x); }
 };
 
+// Exclusive scan of the per-thread pairs over the S time slots of a tile, per channel, in
+// two phases through LDS (thread = slot * NCL + channel lane, VEC channels each; the slots
+// of wave w are w*SPW .. w*SPW+SPW-1).
+//
+// Phase A: every thread stores its pair; lane = channel of each wave then walks that wave's
+// SPW slots in order (backwards for the reverse scan), keeps each slot's exclusive pair within
+// the wave in registers, and stores the wave's aggregate.  No barrier is needed inside phase
+// A: a wave only reads what it has just written, and LDS serves one wave's requests in order.
+// Phase B (after a barrier): lane = channel composes the other waves' aggregates into the
+// wave prefix and stores each slot's exclusive pair for the whole tile.
+// Forward pairs compose earlier first, (P1, E1) o (P2, E2) = (P1 P2, E2 + P2 E1); reverse
+// maps lam_out = P lam_in + E compose the later side first; both reduce to the same update
+// (te, tp) <- (p te + e, tp p) in their own walking order, with the products in GP<CQ>'s
+// representation.
 template <class G, bool REV, bool CQ = false>
 __device__ __forceinline__ void slots_phase_a(const float* P, const float* E, float* sP, float* sE,
                                               float* sWP, float* sWE,
