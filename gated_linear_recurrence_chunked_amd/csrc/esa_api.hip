@@ -129,16 +129,18 @@ int layout_of(const Problem& pr, Layout* L) {
 }
 
 // The block of the reproducible look-back (0 without ESA_DETERMINISTIC): the smallest power
-// of two K with K x (chains of the launch) >= kDetTilesInFlight, at most kDetMaxBlock.  A
-// chain's inclusive values then move K tiles per hop, about as fast as the workgroups in
-// flight on that chain consume tiles, while each tile's walk stays under K words.  It depends
-// on the shape only, so a shape's results are the same on every run.
-constexpr uint64_t kDetTilesInFlight = 64;
+// of two K with K x (chains of the launch) >= kDetBlockTarget, at most kDetMaxBlock.  Few
+// chains need long blocks, or their inclusive values, one hop per block, fall behind the
+// workgroups in flight; long blocks lengthen every tile's walk over its block's aggregates.
+// This rule was the fastest measured from 1 to 512 chains (fp16, bf16, fp32 and fp8).  It
+// depends on the sizes and the storage type only, so a problem's results are the same on
+// every run.
+constexpr uint64_t kDetBlockTarget = 64;
 constexpr uint32_t kDetMaxBlock = 16;
 uint32_t det_block(const Problem& pr, uint32_t nCB) {
     if (!pr.det) return 0;
     uint32_t k = 1;
-    while (k < kDetMaxBlock && (uint64_t)nCB * k < kDetTilesInFlight) k <<= 1;
+    while (k < kDetMaxBlock && (uint64_t)nCB * k < kDetBlockTarget) k <<= 1;
     return k;
 }
 

@@ -659,6 +659,12 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
     }
 }
 
+// Look-back variants, one kernel instance each, so the default kernels carry no code of the
+// others: the default look-back; the reproducible one (ESA_DETERMINISTIC); the forced-timeout
+// test instance (either look-back, chosen at run time, with the chain's first tile withholding
+// its publications and every wait giving up after kTestSpinLimit polls).
+enum : int { kChainDefault = 0, kChainDet = 1, kChainTest = 2 };
+
 // The carry entering `tile` on one lane's chain.  When the neighbouring tile on the earlier
 // side has already published its inclusive value -- the usual case once a chain's earlier
 // tiles were dispatched well before this one -- the tile takes it directly and publishes no
@@ -673,15 +679,10 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
 // values; the others publish their aggregate pair and nothing else (det_publishes_inc).
 // Every word slot then only ever holds one kind of word, so the walk below folds exactly the
 // aggregates back to the nearest publisher and ends at its inclusive value: the carry is the
-// same fp32 expression on every run (bitwise reproducible results), whatever the timing.  K
-// = 1 waits for the neighbour's inclusive value.  The host picks K from the number of chains
-// so that a block's walk stays short while the inclusive values still move K tiles per hop.
-// Look-back variants, one kernel instance each, so the default kernels carry no code of the
-// others: the default look-back; the reproducible one (ESA_DETERMINISTIC); the forced-timeout
-// test instance (either look-back, chosen at run time, with the chain's first tile withholding
-// its publications and every wait giving up after kTestSpinLimit polls).
-enum : int { kChainDefault = 0, kChainDet = 1, kChainTest = 2 };
-
+// same fp32 expression on every run (bitwise reproducible results), whatever the timing.
+// With K = 1 every tile waits for its neighbour's inclusive value.  The host picks K from the
+// number of chains, so that a block's walk stays short while the inclusive values still move
+// K tiles per hop.
 template <bool PROD = false, uint32_t LIMIT = kSpinLimit, bool CQ = false>
 __device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, int64_t nLanes,
                                              int64_t lane, int64_t tile, int step, uint32_t tagAgg,
