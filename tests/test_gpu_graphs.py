@@ -26,10 +26,13 @@ def say(msg):
     sys.stdout.flush()
 
 
+@pytest.mark.parametrize("det", [False, True], ids=["default", "deterministic"])
 @pytest.mark.parametrize("dt,mode", [(torch.float16, "controlled"), (torch.bfloat16, "direct")])
-def test_recorded_scans_replay_correctly(dt, mode):
+def test_recorded_scans_replay_correctly(dt, mode, det):
+    """With ESA_DETERMINISTIC (blocks of 8 tiles on these 8 chains) every replay also gives
+    the eager call's bits."""
     B, T, H, Dh = 4, 3000, 2, 64  # 12 forward and 24 backward tiles per channel block
-    say(f"graph replay {dt} {mode}")
+    say(f"graph replay {dt} {mode} det={det}")
     shp = (B, T, H, Dh)
     x = {k: torch.empty(shp, dtype=dt, device=DEV) for k in ("a", "v", "q", "dy")}
     e0 = synth.random_state(B, H, Dh, 41).to(DEV)
@@ -42,16 +45,18 @@ def test_recorded_scans_replay_correctly(dt, mode):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):  # warm up: the workspace for stream s exists before capture
-        binding.scan_fwd(x["a"], x["v"], x["q"], e0, mode=mode, return_ckpt=True)
+        binding.scan_fwd(x["a"], x["v"], x["q"], e0, mode=mode, return_ckpt=True,
+                         deterministic=det)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        y, eT, ck = binding.scan_fwd(x["a"], x["v"], x["q"], e0, mode=mode, return_ckpt=True)
+        y, eT, ck = binding.scan_fwd(x["a"], x["v"], x["q"], e0, mode=mode, return_ckpt=True,
+                                     deterministic=det)
         da, dv, dq, de0 = binding.scan_bwd(x["a"], x["v"], x["q"], x["dy"], e0, None, ckpt=ck,
-                                           mode=mode)
-        seg_e, seg_p = binding.segment_fwd(x["a"], x["v"], mode=mode)
+                                           mode=mode, deterministic=det)
+        seg_e, seg_p = binding.segment_fwd(x["a"], x["v"], mode=mode, deterministic=det)
 
     for r in range(1, 5):
         fill(r)  # new inputs, written eagerly between replays
@@ -62,10 +67,15 @@ def test_recorded_scans_replay_correctly(dt, mode):
         # eager calls on the same stream and workspace, between replays
         with torch.cuda.stream(s):
             ey, eeT, eck = binding.scan_fwd(x["a"], x["v"], x["q"], e0, mode=mode,
-                                            return_ckpt=True)
+                                            return_ckpt=True, deterministic=det)
             eda, edv, edq, ede0 = binding.scan_bwd(x["a"], x["v"], x["q"], x["dy"], e0, None,
-                                                   ckpt=eck, mode=mode)
+                                                   ckpt=eck, mode=mode, deterministic=det)
+            es_e, es_p = binding.segment_fwd(x["a"], x["v"], mode=mode, deterministic=det)
         torch.cuda.synchronize()
+        if det:
+            for got, ref in ((y, ey), (eT, eeT), (ck, eck), (da, eda), (dv, edv), (dq, edq),
+                             (de0, ede0), (seg_e, es_e), (seg_p, es_p)):
+                assert torch.equal(got, ref), "a deterministic replay differs from eager"
         for name, got, ref in (("y", y, ey), ("d_logit", da, eda), ("d_value", dv, edv),
                                ("d_query", dq, edq)):
             assert_close(f"{name} replay {r} vs eager", got, ref, dt)
