@@ -61,10 +61,10 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         const auto rs_d = make_rsrc(static_cast<const char*>(p.dy) + row0);
 #pragma unroll
         for (int i = 0; i < L; ++i) {
-            ra[i] = ldbuf(rs_a, voff, i * rstride);
-            rv[i] = ldbuf(rs_v, voff, i * rstride);
-            rq[i] = ldbuf(rs_q, voff, i * rstride);
-            rd[i] = ldbuf(rs_d, voff, i * rstride);
+            ra[i] = ldbuf<T>(rs_a, voff, i * rstride);
+            rv[i] = ldbuf<T>(rs_v, voff, i * rstride);
+            rq[i] = ldbuf<T>(rs_q, voff, i * rstride);
+            rd[i] = ldbuf<T>(rs_d, voff, i * rstride);
         }
     } else {
         // ragged tile: rows past the end and lanes past the batch load a clamped, valid
@@ -75,10 +75,10 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         for (int i = 0; i < L; ++i) {
             const int64_t t = t0 + i < p.T ? t0 + i : p.T - 1;
             const int64_t off = (bc * p.T + t) * p.C + cc;
-            ra[i] = ld16(p.a, off, ES);
-            rv[i] = ld16(p.v, off, ES);
-            rq[i] = ld16(p.q, off, ES);
-            rd[i] = ld16(p.dy, off, ES);
+            ra[i] = ld16<T>(p.a, off, ES);
+            rv[i] = ld16<T>(p.v, off, ES);
+            rq[i] = ld16<T>(p.q, off, ES);
+            rd[i] = ld16<T>(p.dy, off, ES);
         }
     }
     // state entering the tile: the initial state, or the forward's checkpoint at the end of
@@ -183,9 +183,9 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         }
         if constexpr (GRADS) {
             if constexpr (FULL)
-                stbuf(static_cast<char*>(p.dq) + row0 + i * rstride, voff, pack<T>(dqv));
+                stbuf<T>(static_cast<char*>(p.dq) + row0 + i * rstride, voff, pack<T>(dqv));
             else if (ok)
-                st16(p.dq, base + i * p.C, ES, pack<T>(dqv));
+                st16<T>(p.dq, base + i * p.C, ES, pack<T>(dqv));
         }
     }
 
@@ -254,11 +254,11 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         }
         if constexpr (GRADS) {
             if constexpr (FULL) {
-                stbuf(static_cast<char*>(p.da) + row0 + i * rstride, voff, pack<T>(dav));
-                stbuf(static_cast<char*>(p.dv) + row0 + i * rstride, voff, pack<T>(dvv));
+                stbuf<T>(static_cast<char*>(p.da) + row0 + i * rstride, voff, pack<T>(dav));
+                stbuf<T>(static_cast<char*>(p.dv) + row0 + i * rstride, voff, pack<T>(dvv));
             } else if (ok) {
-                st16(p.da, base + i * p.C, ES, pack<T>(dav));
-                st16(p.dv, base + i * p.C, ES, pack<T>(dvv));
+                st16<T>(p.da, base + i * p.C, ES, pack<T>(dav));
+                st16<T>(p.dv, base + i * p.C, ES, pack<T>(dvv));
             }
         }
     }

@@ -7,7 +7,8 @@
 // (P1, E1) o (P2, E2) = (P1 P2, E2 + P2 E1) (page "Entangled State Attention",
 // "[ ARCHITECTURE ]", associative composition):
 //
-//   lanes    a thread owns VEC channels (16 bytes of storage) of one (b, t); CB channels
+//   lanes    a thread owns VEC channels (16 bytes of storage, 8 for one-byte storage) of
+//            one (b, t); CB channels
 //            (whole heads, at least 64 channels and 128 bytes) form a channel block,
 //            NCL = CB / VEC threads wide.
 //   tile     a workgroup owns one channel block over TT = S * L time steps: S time slots
@@ -82,12 +83,15 @@ struct f8e5m2 {
 };
 template <>
 struct Storage<f8e4m3> {
-    static constexpr int VEC = 16;
+    static constexpr int VEC = 8;
 };
 template <>
 struct Storage<f8e5m2> {
-    static constexpr int VEC = 16;
+    static constexpr int VEC = 8;
 };
+// Bytes of storage per thread and step: 16 (fp32, fp16, bf16) or 8 (fp8).
+template <typename T>
+constexpr int kVB = Storage<T>::VEC * (int)sizeof(T);
 
 // Tile geometry of a scan kernel instance.  A channel block spans at least 64 channels and at
 // least 128 bytes of each time row: with one-byte storage a 64-channel row piece is 64 bytes,
@@ -112,19 +116,19 @@ struct Geom {
 };
 
 // Per-(dtype, Dh) launch configuration of the forward and backward scans.
-// The forward runs 512-thread workgroups (8 waves): at 64K context a tile is then 256 steps,
-// which halves the look-back words per byte of data against 256 threads and measured ~7 %
-// faster.  The backward holds more per thread (232 VGPRs, 2 waves per SIMD), so a 512-thread
-// workgroup would leave one workgroup per CU; it keeps 256 threads.
-// A thread holds at most 32 elements per step group: four steps of 8 channels, or two steps
-// of 16 channels for one-byte storage (more would spill the backward's registers).  The
-// one-byte forward needs 136 VGPRs, which fit three waves per SIMD: 256-thread workgroups
-// then run three to a CU, measured 1.45x faster at 64K context than one 512-thread
-// workgroup per CU.
+// The forward runs 512-thread workgroups (8 waves): at 64K context a tile is then 256 steps
+// (128 with one-byte storage), which halves the look-back words per byte of data against 256
+// threads and measured ~7 % faster.  The backward holds more per thread (232 VGPRs, 2 waves
+// per SIMD), so a 512-thread workgroup would leave one workgroup per CU; it keeps 256
+// threads.  A thread takes four steps of VEC channels, at most 32 elements (more would spill
+// the backward's registers).  One-byte storage also takes 8 channels per thread, 8 bytes per
+// step: 16 channels over two steps (256-thread forward workgroups, three to a CU) measured 6 %
+// (forward) and 13 % (backward) slower at 64K context, with twice the slot-scan and
+// look-back work per element and 16-channel thread spans whose LDS accesses collide in banks.
 template <typename T, int DH>
 struct FwdCfg {
-    static constexpr int NT = Storage<T>::VEC == 16 ? 256 : 512;
-    static constexpr int L = 32 / Storage<T>::VEC < 4 ? 32 / Storage<T>::VEC : 4;
+    static constexpr int NT = 512;
+    static constexpr int L = 4;
     using G = Geom<T, DH, L, NT>;
 };
 template <typename T, int DH>
@@ -134,8 +138,7 @@ struct BwdCfg {
     // four steps per thread (at least 64 steps per tile): deeper tiles halve the look-back
     // words against two steps per thread and measured ~3 % faster at 64K context, although
     // the 232 VGPRs then allow two waves per SIMD rather than three
-    static constexpr int LR = 32 / Storage<T>::VEC < 4 ? 32 / Storage<T>::VEC : 4;
-    static constexpr int L = LR * S0 >= kCkptChunk ? LR : kCkptChunk / S0;
+    static constexpr int L = 4 * S0 >= kCkptChunk ? 4 : kCkptChunk / S0;
     using G = Geom<T, DH, L, NT>;
     // the backward tile must start on a checkpoint boundary
     static_assert(G::TT % kCkptChunk == 0, "backward tile must be a multiple of 64 steps");
@@ -238,7 +241,8 @@ hipError_t launch_compose(int64_t nseg, int64_t nLanes, int reverse, const float
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 
-// 16 bytes of storage -> VEC fp32 values (exact).
+// VEC values of storage (16 bytes; 8 bytes in x, y for one-byte storage) -> VEC fp32 values
+// (exact).
 template <typename T>
 __device__ __forceinline__ void unpack(const uint4& r, float* out);
 template <>
@@ -268,14 +272,15 @@ __device__ __forceinline__ void unpack<__bf16>(const uint4& r, float* out) {
     }
 }
 
-// One-byte formats: each 32-bit word holds four values, byte k = element k; the packed
-// conversions take or fill the low (false) or high (true) 16-bit half of a word.
+// One-byte formats: a thread's 8 values are the two words x, y; each holds four values, byte
+// k = element k; the packed conversions take or fill the low (false) or high (true) 16-bit
+// half of a word.
 typedef float f2_t __attribute__((ext_vector_type(2)));
 template <bool E5M2>
 __device__ __forceinline__ void unpack_f8(const uint4& r, float* out) {
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    const uint32_t w[2] = {r.x, r.y};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 2; ++k) {
         f2_t lo, hi;
         if constexpr (E5M2) {
             lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w[k], false);
@@ -299,7 +304,7 @@ __device__ __forceinline__ void unpack<f8e5m2>(const uint4& r, float* out) {
     unpack_f8<true>(r, out);
 }
 
-// VEC fp32 values -> 16 bytes of storage (round to nearest even).
+// VEC fp32 values -> VEC values of storage (round to nearest even).
 template <typename T>
 __device__ __forceinline__ uint4 pack(const float* x);
 template <>
@@ -332,9 +337,9 @@ __device__ __forceinline__ uint4 pack<__bf16>(const float* x) {
 // magnitude, infinity for E5M2 beyond 61440.
 template <bool E5M2>
 __device__ __forceinline__ uint4 pack_f8(const float* x) {
-    uint32_t w[4];
+    uint32_t w[2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 2; ++k) {
         int v;
         if constexpr (E5M2) {
             v = __builtin_amdgcn_cvt_pk_bf8_f32(x[4 * k], x[4 * k + 1], 0, false);
@@ -345,7 +350,7 @@ __device__ __forceinline__ uint4 pack_f8(const float* x) {
         }
         w[k] = (uint32_t)v;
     }
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    return make_uint4(w[0], w[1], 0u, 0u);
 }
 template <>
 __device__ __forceinline__ uint4 pack<f8e4m3>(const float* x) {
@@ -372,26 +377,49 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
                                              kBufWord3);
 }
+typedef unsigned int v2u_t __attribute__((ext_vector_type(2)));
+template <typename T>
 __device__ __forceinline__ uint4 ldbuf(__amdgpu_buffer_rsrc_t r, uint32_t voff, int32_t soff) {
-    const v4u_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, kStreamPolicy);
-    return make_uint4(x.x, x.y, x.z, x.w);
+    if constexpr (kVB<T> == 16) {
+        const v4u_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, kStreamPolicy);
+        return make_uint4(x.x, x.y, x.z, x.w);
+    } else {
+        const v2u_t x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, soff, kStreamPolicy);
+        return make_uint4(x.x, x.y, 0u, 0u);
+    }
 }
 // Stores take their row offset in the resource base and a constant scalar offset of 0.  A
 // 16-byte buffer store that names a scalar-register offset gets no wait state before the
 // next instruction overwrites its data registers, and on gfx950 the store can then write
 // the new value for some lanes (seen as corrupted dq rows); with a constant offset the
 // compiler keeps the required gap.
+template <typename T>
 __device__ __forceinline__ void stbuf(const void* row_base, uint32_t voff, const uint4& v) {
-    const v4u_t x = {v.x, v.y, v.z, v.w};
-    __builtin_amdgcn_raw_buffer_store_b128(x, make_rsrc(row_base), (int)voff, 0, kStreamPolicy);
+    if constexpr (kVB<T> == 16) {
+        const v4u_t x = {v.x, v.y, v.z, v.w};
+        __builtin_amdgcn_raw_buffer_store_b128(x, make_rsrc(row_base), (int)voff, 0, kStreamPolicy);
+    } else {
+        const v2u_t x = {v.x, v.y};
+        __builtin_amdgcn_raw_buffer_store_b64(x, make_rsrc(row_base), (int)voff, 0, kStreamPolicy);
+    }
 }
+template <typename T>
 __device__ __forceinline__ uint4 ld16(const void* base, int64_t elem_off, int esize) {
     const char* p = static_cast<const char*>(base) + elem_off * esize;
-    return *reinterpret_cast<const uint4*>(p);
+    if constexpr (kVB<T> == 16) {
+        return *reinterpret_cast<const uint4*>(p);
+    } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        return make_uint4(x.x, x.y, 0u, 0u);
+    }
 }
+template <typename T>
 __device__ __forceinline__ void st16(void* base, int64_t elem_off, int esize, const uint4& v) {
     char* p = static_cast<char*>(base) + elem_off * esize;
-    *reinterpret_cast<uint4*>(p) = v;
+    if constexpr (kVB<T> == 16)
+        *reinterpret_cast<uint4*>(p) = v;
+    else
+        *reinterpret_cast<uint2*>(p) = make_uint2(v.x, v.y);
 }
 
 // Gate: s = sigma(a) = 1 / (1 + exp(-a)) and u = 1 - s = sigma(-a), taken as exp(-a) * s so

@@ -57,9 +57,9 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         const auto rs_v = make_rsrc(static_cast<const char*>(p.v) + row0);
 #pragma unroll
         for (int i = 0; i < L; ++i) {
-            ra[i] = ldbuf(rs_a, voff, i * rstride);
-            rv[i] = ldbuf(rs_v, voff, i * rstride);
-            if constexpr (READOUT) rq[i] = ldbuf(make_rsrc(static_cast<const char*>(p.q) + row0), voff, i * rstride);
+            ra[i] = ldbuf<T>(rs_a, voff, i * rstride);
+            rv[i] = ldbuf<T>(rs_v, voff, i * rstride);
+            if constexpr (READOUT) rq[i] = ldbuf<T>(make_rsrc(static_cast<const char*>(p.q) + row0), voff, i * rstride);
             else rq[i] = make_uint4(0, 0, 0, 0);
         }
     } else {
@@ -71,9 +71,9 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         for (int i = 0; i < L; ++i) {
             const int64_t t = t0 + i < p.T ? t0 + i : p.T - 1;
             const int64_t off = (bc * p.T + t) * p.C + cc;
-            ra[i] = ld16(p.a, off, ES);
-            rv[i] = ld16(p.v, off, ES);
-            if constexpr (READOUT) rq[i] = ld16(p.q, off, ES);
+            ra[i] = ld16<T>(p.a, off, ES);
+            rv[i] = ld16<T>(p.v, off, ES);
+            if constexpr (READOUT) rq[i] = ld16<T>(p.q, off, ES);
             else rq[i] = make_uint4(0, 0, 0, 0);
         }
     }
@@ -199,9 +199,9 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
 #pragma unroll
             for (int e = 0; e < VEC; ++e) yv[e] = qv[e] * (E[e] * r);
             if constexpr (FULL)
-                stbuf(static_cast<char*>(p.y) + row0 + i * rstride, voff, pack<T>(yv));
+                stbuf<T>(static_cast<char*>(p.y) + row0 + i * rstride, voff, pack<T>(yv));
             else if (ok)
-                st16(p.y, base + i * p.C, ES, pack<T>(yv));
+                st16<T>(p.y, base + i * p.C, ES, pack<T>(yv));
         }
         if (ok && p.ckpt && (((t + 1) % kCkptChunk) == 0 || t == p.T - 1)) {
             float* dst = p.ckpt + (ckbase + t / kCkptChunk) * p.C + c;

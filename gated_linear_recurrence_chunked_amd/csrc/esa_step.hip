@@ -24,9 +24,9 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) st[e] = 0.0f;
     if (ok) {
-        ra = ld16(p.a, lane0, ES);
-        rv = ld16(p.v, lane0, ES);
-        rq = ld16(p.q, lane0, ES);
+        ra = ld16<T>(p.a, lane0, ES);
+        rv = ld16<T>(p.v, lane0, ES);
+        rq = ld16<T>(p.q, lane0, ES);
 #pragma unroll
         for (int e = 0; e < VEC; e += 4) {
             const float4 x = *reinterpret_cast<const float4*>(p.state + lane0 + e);
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
         for (int e = 0; e < VEC; e += 4)
             *reinterpret_cast<float4*>(p.state + lane0 + e) =
                 make_float4(st[e], st[e + 1], st[e + 2], st[e + 3]);
-        st16(p.y, lane0, ES, pack<T>(yv));
+        st16<T>(p.y, lane0, ES, pack<T>(yv));
     }
 }
 
