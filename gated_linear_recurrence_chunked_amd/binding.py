@@ -37,7 +37,7 @@ LIB_NAME = "libesa.so"
 
 ESA_OK = 0
 STATUS_NAMES = {0: "ESA_OK", 1: "ESA_ERR_INVALID_ARG", 2: "ESA_ERR_UNSUPPORTED",
-                3: "ESA_ERR_WORKSPACE", 4: "ESA_ERR_HIP"}
+                3: "ESA_ERR_WORKSPACE", 4: "ESA_ERR_HIP", 5: "ESA_ERR_SCRATCH_LIMIT"}
 DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4m3fn: 3,
           torch.float8_e5m2: 4}
 MODES = {"direct": 0, "controlled": 1}
@@ -56,6 +56,7 @@ SIGNATURES = {
     "esa_scan_ckpt_bytes": (_Z, [_I, _I, _I, _I]),
     "esa_workspace_init": (_C, [_P, _Z, _P]),
     "esa_scan_fwd": (_C, [_I, _I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "esa_scan_fwd_noalloc": (_C, [_I, _I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _P, _P, _P]),
     "esa_scan_bwd": (_C, [_I, _I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                           _P, _P, _Z, _P]),
     "esa_state_step": (_C, [_I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _P]),

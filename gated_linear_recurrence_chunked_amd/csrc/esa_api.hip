@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <mutex>
 
 #include "esa.h"
 #include "esa_common.hpp"
@@ -336,7 +337,146 @@ int scan_bwd_impl(bool grads, int64_t B, int64_t T, int64_t H, int64_t Dh, int d
 
 }  // namespace
 
+// ---------------------------------------------------------------------------------------
+// The no-allocation forward (esa_scan_fwd_noalloc): its look-back words live in a static
+// device array instead of a caller's workspace.  Each device that loads the library holds
+// its own copy of the array until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory, so it is never passed to a kernel: at set-up (the
+// first call on a device) hipGetSymbolAddress gives that device's address, which is kept per
+// device and used everywhere the array's memory is needed.
+// ---------------------------------------------------------------------------------------
+static __device__ __attribute__((aligned(256))) uint8_t scratch[ESA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device: the device address of `scratch`, once set up
+
+// The device address of this device's scratch array for a launch on stream s, set up on the
+// first call on that device: the address is looked up with that device current, and the
+// whole array is cleared once (a fill kernel on s; outside graph capture the call waits for
+// it, so that later calls on other streams find it cleared).
+int scratch_for(hipStream_t s, void** out) {
+    int dev = 0;
+    if (s) {
+        if (hipStreamGetDevice(s, &dev) != hipSuccess) return ESA_ERR_HIP;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return ESA_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return ESA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev]) {
+        *out = g_scratch_ptr[dev];
+        return ESA_OK;
+    }
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return ESA_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return ESA_ERR_HIP;
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
+    if (e != hipSuccess || !ptr) return ESA_ERR_HIP;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return ESA_ERR_HIP;
+    if (launch_fill_zero(ptr, ESA_NOALLOC_SCRATCH_BYTES, s) != hipSuccess) return ESA_ERR_HIP;
+    if (cs != hipStreamCaptureStatusActive && hipStreamSynchronize(s) != hipSuccess)
+        return ESA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+    *out = ptr;
+    return ESA_OK;
+}
+
+// The forward with fused readout.  `workspace` is the caller's (workspace_bytes long), or,
+// with `noalloc`, NULL: the look-back words then live in this device's static scratch array.
+int scan_fwd_impl(bool noalloc, int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
+                  const void* gate_logit, const void* value, const void* query,
+                  const float* init_state, void* y, float* final_state, float* ckpt,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    Problem pr;
+    int rc = check_sizes(B, T, H, Dh, dtype, mode, &pr);
+    if (rc != ESA_OK) return rc;
+    rc = check_test_flag(pr, !noalloc);
+    if (rc != ESA_OK) return rc;
+    if (T > 0 && (!gate_logit || !value || !query || !y)) return ESA_ERR_INVALID_ARG;
+    const void* ptrs[] = {gate_logit, value, query, init_state, y, final_state, ckpt, workspace};
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return ESA_ERR_INVALID_ARG;
+    Layout L;
+    rc = layout_of(pr, &L);
+    if (rc != ESA_OK) return rc;
+    const size_t seq = (size_t)(pr.nElem * pr.esize), st = (size_t)(pr.nLanes * 4);
+    const size_t ckb = esa_scan_ckpt_bytes(B, T, H, Dh);
+    const Range in[] = {{gate_logit, seq}, {value, seq}, {query, seq},
+                        {init_state == final_state ? nullptr : init_state, st}};
+    const Range out[] = {{y, seq}, {final_state, st}, {ckpt, ckb}, {workspace, workspace_bytes}};
+    if (any_overlap(in, 4, out, 4)) return ESA_ERR_INVALID_ARG;
+    // look-back words of the forward alone: header, X and Y over the forward's tiles
+    const size_t xbytes = align256((size_t)L.nTilesF * (size_t)pr.nLanes * 8);
+    size_t offY = L.offY;
+    if (noalloc) {
+        if (T > 0 && 256 + 2 * xbytes > (size_t)ESA_NOALLOC_SCRATCH_BYTES) return ESA_ERR_SCRATCH_LIMIT;
+        offY = 256 + xbytes;
+    } else if (T > 0 && (!workspace || workspace_bytes < L.total)) {
+        return ESA_ERR_WORKSPACE;
+    }
+
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (final_state && final_state != init_state)
+            return hip_status(launch_copy_f32(final_state, init_state, pr.nLanes, s));
+        return ESA_OK;
+    }
+    if (noalloc) {
+        rc = scratch_for(s, &workspace);
+        if (rc != ESA_OK) return rc;
+    }
+    char* ws = static_cast<char*>(workspace);
+    FwdParams p;
+    p.a = gate_logit;
+    p.v = value;
+    p.q = query;
+    p.e0 = init_state;
+    p.y = y;
+    p.eT = final_state;
+    p.ckpt = ckpt;
+    p.prod = nullptr;
+    p.hdr = reinterpret_cast<uint32_t*>(ws);
+    p.flagX = reinterpret_cast<uint64_t*>(ws + L.offX);
+    p.flagY = reinterpret_cast<uint64_t*>(ws + offY);
+    p.T = pr.T;
+    p.C = pr.C;
+    p.nLanes = pr.nLanes;
+    p.nck = L.nck;
+    p.nCB = L.nCB;
+    p.nTiles = L.nTilesF;
+    p.det = det_block(pr, L.nCB);
+    p.withhold = pr.forceTimeout;
+    rc = set_epoch(s, p.hdr, &p.epoch, &p.epochWord);
+    if (rc != ESA_OK) return rc;
+    return hip_status(ESA_DISPATCH(fwd, dtype, pr.mode, Dh, p, s));
+}
+
+}  // namespace
+
 extern "C" {
+
+int esa_scan_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
+                 const void* gate_logit, const void* value, const void* query,
+                 const float* init_state, void* y, float* final_state, float* ckpt,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    return scan_fwd_impl(false, B, T, H, Dh, dtype, mode, gate_logit, value, query, init_state, y,
+                         final_state, ckpt, workspace, workspace_bytes, stream);
+}
+
+int esa_scan_fwd_noalloc(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
+                         const void* gate_logit, const void* value, const void* query,
+                         const float* init_state, void* y, float* final_state, float* ckpt,
+                         void* stream) {
+    return scan_fwd_impl(true, B, T, H, Dh, dtype, mode, gate_logit, value, query, init_state, y,
+                         final_state, ckpt, nullptr, 0, stream);
+}
+
 
 int esa_abi_version(void) { return ESA_ABI_VERSION; }
 
@@ -348,6 +488,9 @@ const char* esa_status_string(int status) {
         case ESA_ERR_UNSUPPORTED: return "ESA_ERR_UNSUPPORTED: Dh not in {16, 32, 64, 128} or problem too large";
         case ESA_ERR_WORKSPACE: return "ESA_ERR_WORKSPACE: workspace missing or smaller than esa_scan_workspace_bytes()";
         case ESA_ERR_HIP: return "ESA_ERR_HIP: the HIP runtime rejected a kernel launch";
+        case ESA_ERR_SCRATCH_LIMIT:
+            return "ESA_ERR_SCRATCH_LIMIT: the problem needs more look-back scratch than the "
+                   "no-allocation forward's static array holds (ESA_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown esa_status";
     }
 }
@@ -371,62 +514,6 @@ size_t esa_scan_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t Dh) {
 int esa_workspace_init(void* workspace, size_t bytes, void* stream) {
     if (!workspace || !aligned16(workspace)) return ESA_ERR_INVALID_ARG;
     return hip_status(launch_fill_zero(workspace, bytes, (hipStream_t)stream));
-}
-
-int esa_scan_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
-                 const void* gate_logit, const void* value, const void* query,
-                 const float* init_state, void* y, float* final_state, float* ckpt,
-                 void* workspace, size_t workspace_bytes, void* stream) {
-    Problem pr;
-    int rc = check_sizes(B, T, H, Dh, dtype, mode, &pr);
-    if (rc != ESA_OK) return rc;
-    rc = check_test_flag(pr, true);
-    if (rc != ESA_OK) return rc;
-    if (T > 0 && (!gate_logit || !value || !query || !y)) return ESA_ERR_INVALID_ARG;
-    const void* ptrs[] = {gate_logit, value, query, init_state, y, final_state, ckpt, workspace};
-    for (const void* q : ptrs)
-        if (q && !aligned16(q)) return ESA_ERR_INVALID_ARG;
-    Layout L;
-    rc = layout_of(pr, &L);
-    if (rc != ESA_OK) return rc;
-    const size_t seq = (size_t)(pr.nElem * pr.esize), st = (size_t)(pr.nLanes * 4);
-    const size_t ckb = esa_scan_ckpt_bytes(B, T, H, Dh);
-    const Range in[] = {{gate_logit, seq}, {value, seq}, {query, seq},
-                        {init_state == final_state ? nullptr : init_state, st}};
-    const Range out[] = {{y, seq}, {final_state, st}, {ckpt, ckb}, {workspace, workspace_bytes}};
-    if (any_overlap(in, 4, out, 4)) return ESA_ERR_INVALID_ARG;
-    if (T > 0 && (!workspace || workspace_bytes < L.total)) return ESA_ERR_WORKSPACE;
-
-    hipStream_t s = (hipStream_t)stream;
-    if (T == 0) {
-        if (final_state && final_state != init_state)
-            return hip_status(launch_copy_f32(final_state, init_state, pr.nLanes, s));
-        return ESA_OK;
-    }
-    char* ws = static_cast<char*>(workspace);
-    FwdParams p;
-    p.a = gate_logit;
-    p.v = value;
-    p.q = query;
-    p.e0 = init_state;
-    p.y = y;
-    p.eT = final_state;
-    p.ckpt = ckpt;
-    p.prod = nullptr;
-    p.hdr = reinterpret_cast<uint32_t*>(ws);
-    p.flagX = reinterpret_cast<uint64_t*>(ws + L.offX);
-    p.flagY = reinterpret_cast<uint64_t*>(ws + L.offY);
-    p.T = pr.T;
-    p.C = pr.C;
-    p.nLanes = pr.nLanes;
-    p.nck = L.nck;
-    p.nCB = L.nCB;
-    p.nTiles = L.nTilesF;
-    p.det = det_block(pr, L.nCB);
-    p.withhold = pr.forceTimeout;
-    rc = set_epoch(s, p.hdr, &p.epoch, &p.epochWord);
-    if (rc != ESA_OK) return rc;
-    return hip_status(ESA_DISPATCH(fwd, dtype, pr.mode, Dh, p, s));
 }
 
 int esa_scan_bwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,

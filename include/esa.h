@@ -45,6 +45,8 @@
  *                        exceeds 2^31 - 1
  *   ESA_ERR_WORKSPACE    workspace NULL or smaller than esa_scan_workspace_bytes()
  *   ESA_ERR_HIP          a kernel launch was rejected by the HIP runtime
+ *   ESA_ERR_SCRATCH_LIMIT  (esa_scan_fwd_noalloc only) the problem needs more look-back
+ *                        scratch than ESA_NOALLOC_SCRATCH_BYTES
  */
 #ifndef ESA_H
 #define ESA_H
@@ -58,8 +60,9 @@ extern "C" {
 
 /* 1: fp32 / fp16 / bf16 storage.  2: adds the fp8 storage dtypes ESA_F8E4M3, ESA_F8E5M2,
  * the sequence-segment calls and the ESA_DETERMINISTIC mode flag.  3: adds the
- * ESA_TEST_FORCE_TIMEOUT mode flag. */
-#define ESA_ABI_VERSION 3
+ * ESA_TEST_FORCE_TIMEOUT mode flag.  4: adds esa_scan_fwd_noalloc and
+ * ESA_ERR_SCRATCH_LIMIT. */
+#define ESA_ABI_VERSION 4
 
 /* Checkpoint granularity: the forward can store the fp32 state at every 64th step. */
 #define ESA_CKPT_CHUNK 64
@@ -69,7 +72,8 @@ typedef enum {
     ESA_ERR_INVALID_ARG = 1,
     ESA_ERR_UNSUPPORTED = 2,
     ESA_ERR_WORKSPACE = 3,
-    ESA_ERR_HIP = 4
+    ESA_ERR_HIP = 4,
+    ESA_ERR_SCRATCH_LIMIT = 5
 } esa_status;
 
 /* Storage dtype of the sequence tensors (precision modes of page "Entangled State
@@ -153,6 +157,33 @@ int esa_scan_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mod
                  const void *gate_logit, const void *value, const void *query,
                  const float *init_state, void *y, float *final_state, float *ckpt,
                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- The forward without a workspace, for callers that cannot allocate ----
+ *
+ * For code that may not call hipMalloc (work recorded into a HIP graph, tight serving
+ * loops, harnesses that forbid allocation): esa_scan_fwd with the same arguments, minus the
+ * workspace.  Its look-back words live in a static device array of ESA_NOALLOC_SCRATCH_BYTES
+ * that every device the library runs on holds until the process ends; the call allocates
+ * nothing.  The problem needs 256 + 2 * ceil(T / TT) * B * H * Dh * 8 bytes of it, TT being
+ * the forward's tile length in steps: 256 (16-bit storage, Dh <= 64), 128 (16-bit with
+ * Dh = 128, 8-bit, fp32 with Dh <= 64) or 64 (fp32 with Dh = 128);
+ * esa_scan_workspace_bytes() of the same problem is an upper bound.  Larger
+ * problems get ESA_ERR_SCRATCH_LIMIT before anything is launched.  Example: B = 256,
+ * T = 8192, H = 8, Dh = 64 in fp16 needs 64 MiB + 256 bytes and is refused; T = 4096 fits.
+ *
+ * The first call on a device looks up that device's copy of the array and clears it once
+ * (a fill kernel on `stream`; outside graph capture that first call then waits for the
+ * stream).  Every later call on the device reuses the array as it was left.  All calls on one
+ * device share the one array: calls that overlap in time on one device race (run them on
+ * one stream, or one after another); replays of graphs that recorded this call count as
+ * calls.  ESA_DETERMINISTIC is accepted; ESA_TEST_FORCE_TIMEOUT is refused
+ * (ESA_ERR_INVALID_ARG).  Arguments, results and the other errors are those of
+ * esa_scan_fwd. */
+#define ESA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int esa_scan_fwd_noalloc(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode,
+                         const void *gate_logit, const void *value, const void *query,
+                         const float *init_state, void *y, float *final_state, float *ckpt,
+                         void *stream);
 
 /* Backward of esa_scan_fwd: the chain rule through readout, recurrence and gate, run as a
  * reverse-time scan dE_t = gE_t + s_{t+1} dE_{t+1} (no page states it; it is derived from

@@ -47,7 +47,7 @@ def header_abi_version() -> int:
 
 
 def test_version_and_status_strings(lib):
-    assert lib.esa_abi_version() == header_abi_version() == 3
+    assert lib.esa_abi_version() == header_abi_version() == 4
     for s in range(5):
         assert lib.esa_status_string(s).decode().startswith(
             ["ESA_OK", "ESA_ERR_INVALID_ARG", "ESA_ERR_UNSUPPORTED", "ESA_ERR_WORKSPACE",
