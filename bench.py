@@ -212,34 +212,27 @@ def bench_decode(args, torch, binding, synth):
         torch.cuda.empty_cache()
     sps = [v["decode_steps_per_s"] for v in res["prefill"].values()]
     res["decode_steps_per_s"] = sum(sps) / len(sps)
-    # the same chain of steps captured once into a HIP graph and replayed (no per-launch
-    # host work); the step kernel records no memset node
-    st_g = st.clone()
-    ys_g = torch.empty((B, H, Dh), dtype=torch.float16, device="cuda:0")
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for s in steps[:4]:
-            binding.state_step(s["a"], s["v"], s["q"], st_g.clone(), mode=wl.mode, y=ys_g)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for s in steps:
-            binding.state_step(s["a"], s["v"], s["q"], st_g, mode=wl.mode, y=ys_g)
-    graph.replay()
+    # the same chain of steps recorded once into a HIP graph (binding.DecodeGraph, which owns
+    # the buffers it replays) and replayed from the last prefill's state: no host work per step
+    dg = binding.DecodeGraph(B, H, Dh, n, dtype=torch.float16, mode=wl.mode, device="cuda:0")
+    for k, s in enumerate(steps):
+        dg.a[k].copy_(s["a"])
+        dg.v[k].copy_(s["v"])
+        dg.q[k].copy_(s["q"])
+    dg.state.copy_(st)
+    dg.replay()
     torch.cuda.synchronize()
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 3
     g0.record()
     for _ in range(reps):
-        graph.replay()
+        dg.replay()
     g1.record()
     torch.cuda.synchronize()
     gms = g0.elapsed_time(g1) / reps
     res["decode_graph_us_per_step"] = gms * 1e3 / n
     res["decode_graph_steps_per_s"] = n / (gms * 1e-3)
-    del graph
+    del dg
     res["decode_tokens_per_s"] = res["decode_steps_per_s"] * B
     res["decode_graph_tokens_per_s"] = res["decode_graph_steps_per_s"] * B
     res["decode_step_bytes"] = B * H * Dh * (4 * 2 + 2 * 4)

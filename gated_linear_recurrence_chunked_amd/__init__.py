@@ -7,9 +7,10 @@ does, and fails loudly when the library is missing.
 """
 from __future__ import annotations
 
-_BINDING = ["scan_fwd", "scan_bwd", "state_step", "StepPlan", "segment_fwd", "segment_bwd",
-            "segment_compose", "workspace_bytes", "ckpt_bytes", "EsaError", "library_path",
-            "load_library"]
+_BINDING = ["scan_fwd", "scan_bwd", "state_step", "StepPlan", "DecodeGraph", "segment_fwd",
+            "segment_bwd", "segment_compose", "workspace_bytes", "ckpt_bytes", "EsaError",
+            "library_path", "load_library", "workspace_status", "check_timeouts",
+            "set_timeout_checks"]
 _AUTOGRAD = ["esa_scan", "ESALayer"]
 __all__ = _BINDING + _AUTOGRAD
 

@@ -36,13 +36,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libesa.so"
 
 ESA_OK = 0
+ESA_ERR_TIMEOUT = 6
 STATUS_NAMES = {0: "ESA_OK", 1: "ESA_ERR_INVALID_ARG", 2: "ESA_ERR_UNSUPPORTED",
-                3: "ESA_ERR_WORKSPACE", 4: "ESA_ERR_HIP", 5: "ESA_ERR_SCRATCH_LIMIT"}
+                3: "ESA_ERR_WORKSPACE", 4: "ESA_ERR_HIP", 5: "ESA_ERR_SCRATCH_LIMIT",
+                6: "ESA_ERR_TIMEOUT"}
 DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4m3fn: 3,
           torch.float8_e5m2: 4}
 MODES = {"direct": 0, "controlled": 1}
 DETERMINISTIC = 0x100  # ESA_DETERMINISTIC: OR-ed into the mode, bitwise reproducible scans
 TEST_FORCE_TIMEOUT = 0x200  # ESA_TEST_FORCE_TIMEOUT: a look-back timeout forced for tests
+LOOKBACK_STATS = 0x400  # ESA_LOOKBACK_STATS: the kernel instance that counts look-back walks
 
 # every function include/esa.h declares: name -> (restype, argtypes)
 _P = ctypes.c_void_p
@@ -55,6 +58,7 @@ SIGNATURES = {
     "esa_scan_workspace_bytes": (_Z, [_I, _I, _I, _I, _C]),
     "esa_scan_ckpt_bytes": (_Z, [_I, _I, _I, _I]),
     "esa_workspace_init": (_C, [_P, _Z, _P]),
+    "esa_workspace_status": (_C, [_P, ctypes.POINTER(ctypes.c_uint32), _P]),
     "esa_scan_fwd": (_C, [_I, _I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "esa_scan_fwd_noalloc": (_C, [_I, _I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _P, _P, _P]),
     "esa_scan_bwd": (_C, [_I, _I, _I, _I, _C, _C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -69,6 +73,11 @@ SIGNATURES = {
 _lock = threading.Lock()
 _lib = None
 _workspaces: dict = {}
+# Workspaces replaced by larger ones.  A HIP graph that recorded a scan keeps the raw address
+# of the workspace it ran on and uses it on every replay, so a workspace is never freed once
+# it has served a call: a superseded one stays alive here for the life of the process.
+_retired: list = []
+_check_each_call = os.environ.get("ESA_CHECK_TIMEOUTS", "") not in ("", "0")
 
 
 def library_path() -> str:
@@ -159,9 +168,66 @@ def get_workspace(nbytes: int, device) -> torch.Tensor:
     key = (index, _raw_stream(index))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _retired.append(ws)  # a captured graph may still use it (see _retired)
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=torch.device("cuda", index))
         _workspaces[key] = ws
     return ws
+
+
+STAT_NAMES = ("took_published", "walked", "tiles_folded", "longest_walk", "polls")
+
+
+def workspace_status(workspace=None, stream=None) -> dict:
+    """What a workspace's header records (esa_workspace_status; waits for the stream): the
+    tag of the last scan launch whose cross-tile wait timed out (0: none since the workspace
+    was initialised) and the look-back counters of ESA_LOOKBACK_STATS launches.  `workspace`
+    is a workspace tensor, or None for the current device's no-allocation scratch."""
+    lib = load_library()
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+            raise ValueError("workspace must be a CUDA (HIP) tensor")
+        index = workspace.device.index
+        ptr = workspace.data_ptr()
+    else:
+        index = torch.cuda.current_device()
+        ptr = None
+    if stream is None:
+        stream = _raw_stream(index)
+    info = (ctypes.c_uint32 * 6)()
+    st = lib.esa_workspace_status(ptr, info, stream)
+    if st not in (ESA_OK, ESA_ERR_TIMEOUT):
+        _check(st, "esa_workspace_status")
+    out = {"timeout_tag": int(info[0])}
+    out.update({n: int(info[1 + k]) for k, n in enumerate(STAT_NAMES)})
+    return out
+
+
+def _raise_if_timed_out(ws: torch.Tensor, where: str):
+    """Reads the workspace's timeout record (waiting for its stream); if a launch timed out,
+    clears the record, so that each timeout is reported once, and raises EsaError."""
+    if workspace_status(ws)["timeout_tag"]:
+        ws[12:16].zero_()
+        raise EsaError(ESA_ERR_TIMEOUT, where)
+
+
+def check_timeouts():
+    """Waits for the binding's workspaces' streams and raises EsaError (ESA_ERR_TIMEOUT) if a
+    scan launched on one of them had a cross-tile wait time out since the last check; its
+    outputs that depended on the missing value are NaN.  Never happens in a correct run."""
+    for (index, stream), ws in list(_workspaces.items()):
+        with torch.cuda.device(index):
+            if workspace_status(ws, stream)["timeout_tag"]:
+                ws[12:16].zero_()
+                raise EsaError(ESA_ERR_TIMEOUT, f"scan on device {index}")
+
+
+def set_timeout_checks(on: bool = True):
+    """Debug mode (also set by the environment variable ESA_CHECK_TIMEOUTS=1): after every
+    scan call, wait for it and raise EsaError if its cross-tile wait timed out.  Each check
+    synchronises the stream."""
+    global _check_each_call
+    _check_each_call = bool(on)
 
 
 _ws_need: dict = {}
@@ -196,6 +262,8 @@ def scan_fwd(a, v, q, init_state=None, mode="controlled", return_ckpt=False, fin
                                             bool(return_ckpt), final_state, y, ws)
     if st:
         _check(st, "esa_scan_fwd")
+    if _check_each_call:
+        _raise_if_timed_out(ws, "esa_scan_fwd")
     if return_ckpt:
         return y, final_state, ckpt
     return y, final_state
@@ -213,6 +281,8 @@ def scan_bwd(a, v, q, dy, init_state=None, d_final_state=None, ckpt=None, mode="
                                           d_query, d_init)
     if st:
         _check(st, "esa_scan_bwd")
+    if _check_each_call:
+        _raise_if_timed_out(ws, "esa_scan_bwd")
     return da, dv, dq, d_init
 
 
@@ -242,6 +312,8 @@ def segment_fwd(a, v, mode="controlled", workspace=None, deterministic=False):
     st, seg_state, seg_prod = ext.segment_fwd(a, v, _mode(mode, deterministic), ws)
     if st:
         _check(st, "esa_scan_segment_fwd")
+    if _check_each_call:
+        _raise_if_timed_out(ws, "esa_scan_segment_fwd")
     return seg_state, seg_prod
 
 
@@ -255,6 +327,8 @@ def segment_bwd(a, v, q, dy, init_state=None, ckpt=None, mode="controlled", work
                                      ws)
     if st:
         _check(st, "esa_scan_segment_bwd")
+    if _check_each_call:
+        _raise_if_timed_out(ws, "esa_scan_segment_bwd")
     return seg_d_init
 
 
@@ -306,3 +380,79 @@ class StepPlan:
         if st:
             _check(st, "esa_state_step")
         return y
+
+
+class DecodeGraph:
+    """A chain of `steps` one-token updates (esa_state_step) recorded once into a HIP graph and
+    replayed with no host work per step: generation's decode loop without the per-launch
+    cost (page "Entangled State Attention v2.1", sections 5 and 6: the step-wise decode
+    interface and compiled generation).
+
+    A graph replays fixed addresses, so the object owns every buffer its steps read and write:
+
+        state      fp32 [B, H, Dh]            the recurrent state, updated in place by each step
+        a, v, q    dtype [steps, B, H, Dh]    the steps' gate logits, values and queries
+        y          dtype [steps, B, H, Dh]    each step's readout
+        snapshots  fp32 [len(snapshot_steps), B, H, Dh]  the state after each listed step
+                   (1-based: 1 is the state after the first step)
+
+    Write the inputs and the starting state, then replay():
+
+        dg = DecodeGraph(B, H, Dh, steps=1, dtype=torch.float16)   # one token per replay
+        dg.state.copy_(prefill_state)
+        for t in ...:
+            dg.a[0].copy_(a_t); dg.v[0].copy_(v_t); dg.q[0].copy_(q_t)
+            dg.replay()                                            # y_t in dg.y[0]
+
+    With steps = n > 1 one replay runs n steps whose inputs are all known beforehand (teacher
+    forcing, or timing).  Replays run on the current stream; a replay must not overlap another
+    replay of the same object or eager use of its buffers.
+    """
+
+    def __init__(self, B, H, Dh, steps, dtype=torch.float16, mode="controlled", device=None,
+                 snapshot_steps=()):
+        if dtype not in DTYPES:
+            raise TypeError(f"dtype {dtype} not supported")
+        if steps < 1:
+            raise ValueError("steps must be at least 1")
+        snaps = tuple(int(k) for k in snapshot_steps)
+        if any(k < 1 or k > steps for k in snaps):
+            raise ValueError(f"snapshot steps must lie in 1..{steps}")
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else \
+            torch.device(device)
+        ext = _torch_ext()
+        self.steps, self.dtype, self.mode = steps, dtype, _mode(mode)
+        self.state = torch.zeros((B, H, Dh), dtype=torch.float32, device=dev)
+        shp = (steps, B, H, Dh)
+        self.a = torch.zeros(shp, dtype=dtype, device=dev)
+        self.v = torch.zeros(shp, dtype=dtype, device=dev)
+        self.q = torch.zeros(shp, dtype=dtype, device=dev)
+        self.y = torch.empty(shp, dtype=dtype, device=dev)
+        self.snapshots = torch.empty((len(snaps), B, H, Dh), dtype=torch.float32, device=dev)
+        after = {}
+        for i, k in enumerate(snaps):
+            after.setdefault(k - 1, []).append(i)
+        # one eager step on a copy of the state, on the capture stream, before recording
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            st = ext.state_step(self.state.clone(), self.a[0], self.v[0], self.q[0], self.y[0],
+                                self.mode)
+            if st:
+                _check(st, "esa_state_step")
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize(dev)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph, stream=side):
+            for k in range(steps):
+                st = ext.state_step(self.state, self.a[k], self.v[k], self.q[k], self.y[k],
+                                    self.mode)
+                if st:
+                    _check(st, "esa_state_step")
+                for i in after.get(k, ()):
+                    self.snapshots[i].copy_(self.state)
+        torch.cuda.synchronize(dev)
+
+    def replay(self):
+        """Runs the recorded steps on the current stream."""
+        self.graph.replay()

@@ -21,6 +21,7 @@ struct Problem {
     int dtype, mode;  // mode: the recurrence form (ESA_DIRECT / ESA_CONTROLLED)
     uint32_t det;     // ESA_DETERMINISTIC was set
     uint32_t forceTimeout;  // ESA_TEST_FORCE_TIMEOUT was set
+    uint32_t stats;   // ESA_LOOKBACK_STATS was set
     int64_t esize;
 };
 
@@ -71,7 +72,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int check_sizes(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode, Problem* pr) {
-    const int form = mode & ~(ESA_DETERMINISTIC | ESA_TEST_FORCE_TIMEOUT);
+    const int form = mode & ~(ESA_DETERMINISTIC | ESA_TEST_FORCE_TIMEOUT | ESA_LOOKBACK_STATS);
     if (dtype < ESA_F32 || dtype > ESA_F8E5M2 || form < ESA_DIRECT || form > ESA_CONTROLLED)
         return ESA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || Dh < 1 || T < 0) return ESA_ERR_INVALID_ARG;
@@ -84,6 +85,7 @@ int check_sizes(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode
     pr->mode = form;
     pr->det = (mode & ESA_DETERMINISTIC) ? 1u : 0u;
     pr->forceTimeout = (mode & ESA_TEST_FORCE_TIMEOUT) ? 1u : 0u;
+    pr->stats = (mode & ESA_LOOKBACK_STATS) ? 1u : 0u;
     pr->esize = storage_bytes(dtype);
     int64_t bytes;
     if (!mul64(H, Dh, &pr->C) || !mul64(B, pr->C, &pr->nLanes) || !mul64(pr->nLanes, T, &pr->nElem) ||
@@ -94,7 +96,16 @@ int check_sizes(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mode
 
 // ESA_TEST_FORCE_TIMEOUT is accepted by the readout forward and the gradient backward, for
 // fp16 storage and Dh = 64 (the problems with a test instance of the kernels).
+//
+// ESA_LOOKBACK_STATS likewise, for fp16 and fp8 E4M3 storage with Dh = 64; it cannot be
+// combined with ESA_DETERMINISTIC or ESA_TEST_FORCE_TIMEOUT (the statistics count the
+// default look-back).
 int check_test_flag(const Problem& pr, bool call_allows_it) {
+    if (pr.stats) {
+        if (!call_allows_it || pr.det || pr.forceTimeout) return ESA_ERR_INVALID_ARG;
+        if (!((pr.dtype == ESA_F16 || pr.dtype == ESA_F8E4M3) && pr.Dh == 64))
+            return ESA_ERR_UNSUPPORTED;
+    }
     if (!pr.forceTimeout) return ESA_OK;
     if (!call_allows_it) return ESA_ERR_INVALID_ARG;
     return pr.dtype == ESA_F16 && pr.Dh == 64 ? ESA_OK : ESA_ERR_UNSUPPORTED;
@@ -330,6 +341,7 @@ int scan_bwd_impl(bool grads, int64_t B, int64_t T, int64_t H, int64_t Dh, int d
     p.nTiles = L.nTilesB;
     p.det = det_block(pr, L.nCB);
     p.withhold = pr.forceTimeout;
+    p.stats = pr.stats;
     rc = set_epoch(s, hdr, &p.epoch, &p.epochWord);
     if (rc != ESA_OK) return rc;
     return hip_status(ESA_DISPATCH(bwd, dtype, pr.mode, Dh, p, s));
@@ -452,6 +464,7 @@ int scan_fwd_impl(bool noalloc, int64_t B, int64_t T, int64_t H, int64_t Dh, int
     p.nTiles = L.nTilesF;
     p.det = det_block(pr, L.nCB);
     p.withhold = pr.forceTimeout;
+    p.stats = pr.stats;
     rc = set_epoch(s, p.hdr, &p.epoch, &p.epochWord);
     if (rc != ESA_OK) return rc;
     return hip_status(ESA_DISPATCH(fwd, dtype, pr.mode, Dh, p, s));
@@ -488,6 +501,9 @@ const char* esa_status_string(int status) {
         case ESA_ERR_UNSUPPORTED: return "ESA_ERR_UNSUPPORTED: Dh not in {16, 32, 64, 128} or problem too large";
         case ESA_ERR_WORKSPACE: return "ESA_ERR_WORKSPACE: workspace missing or smaller than esa_scan_workspace_bytes()";
         case ESA_ERR_HIP: return "ESA_ERR_HIP: the HIP runtime rejected a kernel launch";
+        case ESA_ERR_TIMEOUT:
+            return "ESA_ERR_TIMEOUT: a cross-tile wait of a scan on this workspace timed out; "
+                   "the outputs that depend on it are NaN";
         case ESA_ERR_SCRATCH_LIMIT:
             return "ESA_ERR_SCRATCH_LIMIT: the problem needs more look-back scratch than the "
                    "no-allocation forward's static array holds (ESA_NOALLOC_SCRATCH_BYTES)";
@@ -509,6 +525,41 @@ size_t esa_scan_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t Dh) {
     int64_t n;
     if (!mul64(cdiv(T, kCkptChunk), pr.nLanes, &n) || !mul64(n, 4, &n)) return 0;
     return (size_t)n;
+}
+
+int esa_workspace_status(const void* workspace, uint32_t* info, void* stream) {
+    if (!info || (workspace && !aligned16(workspace))) return ESA_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return ESA_ERR_HIP;
+    if (cs != hipStreamCaptureStatusNone) return ESA_ERR_INVALID_ARG;  // it waits for the stream
+    const void* src = workspace;
+    if (!src) {  // this device's no-allocation scratch, if a call has set it up
+        int dev = 0;
+        if (s ? hipStreamGetDevice(s, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+            return ESA_ERR_HIP;
+        if (dev < 0 || dev >= kMaxDevices) return ESA_ERR_UNSUPPORTED;
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        src = g_scratch_ptr[dev];
+    }
+    uint32_t h[64] = {0};
+    if (src) {
+        if (hipMemcpyAsync(h, src, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return ESA_ERR_HIP;
+    }
+    uint32_t sum[kStatWords] = {0};
+    for (int x = 0; x < 8; ++x)
+        for (int k = 0; k < kStatWords; ++k) {
+            const uint32_t v = h[kStatWordsOffset + x * kStatWords + k];
+            if (k == kStatMaxWalk)
+                sum[k] = v > sum[k] ? v : sum[k];
+            else
+                sum[k] += v;
+        }
+    info[0] = h[3];
+    for (int k = 0; k < kStatWords; ++k) info[1 + k] = sum[k];
+    return h[3] ? ESA_ERR_TIMEOUT : ESA_OK;
 }
 
 int esa_workspace_init(void* workspace, size_t bytes, void* stream) {

@@ -214,24 +214,29 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         tile_total<G, true, CQ>(sWP, sWE, ch, tp, te);
         const int64_t gl = (int64_t)cb * CB + ch;
         float carry = 0.0f;
+        constexpr bool STATS = CHAIN == kChainStats;
+        WalkCount wc{~0u, 0u};  // statistics instance: set when the lane walked back
+        bool active = false;
         if (FULL || gl < p.nLanes) {
             uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
             constexpr bool TEST = CHAIN == kChainTest;
-            const uint32_t det = CHAIN == kChainDefault ? 0u : p.det;
+            const uint32_t det = CHAIN == kChainDet || TEST ? p.det : 0u;
             const bool inc = det_publishes_inc(p.nTiles - 1 - tile, det);
             if (tile == p.nTiles - 1) {
                 carry = p.dET ? p.dET[gl] : 0.0f;
             } else {
                 float pin;  // unused: the backward carries no gate product
+                active = true;
                 carry = chain_carry<false, TEST ? kTestSpinLimit : kSpinLimit, CQ>(
                     p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc, p.hdr, tp, te, &pin,
-                    det, inc);
+                    det, inc, STATS ? &wc : nullptr);
             }
             const float lam_out = te + Q::apply(tp, carry);
             // the test instance withholds the last tile
             if ((!TEST || tile != p.nTiles - 1) && inc) publish(X, tagInc, lam_out);
             if (tile == 0 && p.de0) p.de0[gl] = lam_out;
         }
+        if constexpr (STATS) count_walks(p.hdr, active, wc.folded != ~0u, wc);
         sCarry[ch] = carry;
     }
     __syncthreads();
@@ -307,6 +312,18 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
         if constexpr (std::is_same<T, _Float16>::value && DH == 64) {
             using C = BwdCfg<T, DH>;
             hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT, true, kChainTest>),
+                               dim3(p.nCB * p.nTiles), dim3(C::NT), 0, s, p);
+            return hipGetLastError();
+        } else {
+            return hipErrorNotSupported;
+        }
+    }
+    if (p.da && p.stats) {
+        // the look-back statistics instance: fp16 and fp8 E4M3 storage with Dh = 64
+        if constexpr ((std::is_same<T, _Float16>::value || std::is_same<T, f8e4m3>::value) &&
+                      DH == 64) {
+            using C = BwdCfg<T, DH>;
+            hipLaunchKernelGGL((bwd_kernel<T, MODE, DH, C::L, C::NT, true, kChainStats>),
                                dim3(p.nCB * p.nTiles), dim3(C::NT), 0, s, p);
             return hipGetLastError();
         } else {

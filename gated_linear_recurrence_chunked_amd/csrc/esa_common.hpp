@@ -148,9 +148,21 @@ struct BwdCfg {
 struct WsHeader {
     uint32_t epoch;  // device epoch of launches recorded into graphs (bit 29 set once used)
     uint32_t reserved[2];
-    uint32_t abort;  // sticky: set when a look-back wait timed out (results are then NaN)
-    uint32_t pad[60];
+    // 0, or the inclusive tag of the last launch whose look-back wait timed out (its results
+    // that depend on the missing value are NaN); only waits of that launch give up on it
+    uint32_t abort;
+    uint32_t pad0[4];
+    // look-back statistics, counted by the statistics instance only (kChainStats): 8 sets
+    // (workgroup ID mod 8, i.e. one per XCD) of kStatWords counters, see LbStat
+    uint32_t stats[8 * 5];
+    uint32_t pad[16];
 };
+constexpr int kStatWordsOffset = 8;  // header word of stats[0]
+// Counters of one statistics set: lanes whose neighbouring tile already showed its inclusive
+// value; lanes that walked back; earlier tiles folded during walks; the longest walk (tiles
+// folded plus the inclusive value that ended it); unproductive polls.
+enum LbStat : int { kStatTook = 0, kStatWalked = 1, kStatFolded = 2, kStatMaxWalk = 3,
+                    kStatPolls = 4, kStatWords = 5 };
 constexpr uint32_t kHostEpochMask = 0x1fffffffu;  // host epochs: bit 29 clear
 constexpr uint32_t kDeviceEpochBit = 0x20000000u;  // device epochs: bit 29 set
 static_assert(sizeof(WsHeader) == 256, "header must be 256 bytes");
@@ -180,6 +192,7 @@ struct FwdParams {
     const uint32_t* epochWord;  // non-NULL: read the epoch here instead (graph-recorded launch)
     uint32_t det;    // 0, or the block of the reproducible look-back (a power of two)
     uint32_t withhold;  // non-zero: launch the forced-timeout test instance (see launch_fwd)
+    uint32_t stats;     // non-zero: launch the look-back statistics instance
 };
 
 struct BwdParams {
@@ -207,6 +220,7 @@ struct BwdParams {
     const uint32_t* epochWord;
     uint32_t det;
     uint32_t withhold;
+    uint32_t stats;
 };
 
 struct StepParams {
@@ -635,15 +649,18 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 // gives up after kTestSpinLimit polls.
 constexpr uint32_t kTestSpinLimit = 4096;
 
-// One unproductive poll of a bounded wait: false once the wait must give up (the workspace's
-// abort word is set, or this wait has polled LIMIT times; then it sets the abort word).
+// One unproductive poll of a bounded wait: false once the wait must give up (this launch's
+// tag is in the abort word, or this wait has polled LIMIT times; then it puts it there).  The
+// abort word holds the tag of the launch that timed out, so a timeout never makes the waits
+// of later launches on the same workspace give up.
 template <uint32_t LIMIT = kSpinLimit>
-__device__ __forceinline__ bool wait_turn(uint32_t polls, uint32_t* hdr) {
+__device__ __forceinline__ bool wait_turn(uint32_t polls, uint32_t* hdr, uint32_t abortTag) {
     if ((polls & 255u) == 0u) {
-        const bool abort =
-            __hip_atomic_load(&hdr[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+        const bool abort = __hip_atomic_load(&hdr[3], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) == abortTag;
         if (abort || polls >= LIMIT) {
-            if (!abort) __hip_atomic_store(&hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (!abort)
+                __hip_atomic_store(&hdr[3], abortTag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return false;
         }
     }
@@ -651,11 +668,18 @@ __device__ __forceinline__ bool wait_turn(uint32_t polls, uint32_t* hdr) {
     return true;
 }
 
+// What one lane's walk did, for the statistics instance: earlier tiles folded, unproductive
+// polls.
+struct WalkCount {
+    uint32_t folded;
+    uint32_t polls;
+};
+
 template <bool PROD = false, uint32_t LIMIT = kSpinLimit, bool CQ = false>
 __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t* flagY,
                                            int64_t nLanes, int64_t lane, int64_t tile, int step,
                                            uint32_t tagAgg, uint32_t tagInc, uint32_t* hdr,
-                                           float* pinc = nullptr) {
+                                           float* pinc = nullptr, WalkCount* wc = nullptr) {
     static_assert(!(PROD && CQ), "the gate product of a segment is carried as itself");
     float ap = GP<CQ>::one, ae = 0.0f;
     int64_t j = tile + step;
@@ -666,7 +690,10 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
         const uint64_t yv = peek(flagY + j * nLanes + lane);
         const uint32_t tg = word_tag(x);
         if (tg == tagInc) {
-            if constexpr (!PROD) return ae + GP<CQ>::apply(ap, word_val(x));
+            if constexpr (!PROD) {
+                if (wc) *wc = WalkCount{(uint32_t)((j - tile) * step - 1), polls};
+                return ae + GP<CQ>::apply(ap, word_val(x));
+            }
             // the inclusive product is published beside the inclusive state, in no fixed
             // order: wait until it is visible too
             if (word_tag(yv) == tagInc) {
@@ -680,8 +707,9 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
             j += step;
             continue;
         }
-        if (!wait_turn<LIMIT>(++polls, hdr)) {
+        if (!wait_turn<LIMIT>(++polls, hdr, tagInc)) {
             if constexpr (PROD) *pinc = __builtin_nanf("");
+            if (wc) *wc = WalkCount{(uint32_t)((j - tile) * step - 1), polls};
             return __builtin_nanf("");
         }
     }
@@ -691,7 +719,8 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
 // others: the default look-back; the reproducible one (ESA_DETERMINISTIC); the forced-timeout
 // test instance (either look-back, chosen at run time, with the chain's first tile withholding
 // its publications and every wait giving up after kTestSpinLimit polls).
-enum : int { kChainDefault = 0, kChainDet = 1, kChainTest = 2 };
+// The statistics instance (kChainStats) is the default look-back with counters (LbStat).
+enum : int { kChainDefault = 0, kChainDet = 1, kChainTest = 2, kChainStats = 3 };
 
 // The carry entering `tile` on one lane's chain.  When the neighbouring tile on the earlier
 // side has already published its inclusive value -- the usual case once a chain's earlier
@@ -715,7 +744,8 @@ template <bool PROD = false, uint32_t LIMIT = kSpinLimit, bool CQ = false>
 __device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, int64_t nLanes,
                                              int64_t lane, int64_t tile, int step, uint32_t tagAgg,
                                              uint32_t tagInc, uint32_t* hdr, float tp, float te,
-                                             float* pin, uint32_t det, bool pubInc) {
+                                             float* pin, uint32_t det, bool pubInc,
+                                             WalkCount* wc = nullptr) {
     if (det == 0u) {
         const uint64_t x = peek(flagX + (tile + step) * nLanes + lane);
         if (word_tag(x) == tagInc) {
@@ -731,8 +761,37 @@ __device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, i
         publish(flagX + tile * nLanes + lane, tagAgg, te);
         publish(flagY + tile * nLanes + lane, tagAgg, tp);
     }
+    if (wc) *wc = WalkCount{0u, 0u};
     return look_back<PROD, LIMIT, CQ>(flagX, flagY, nLanes, lane, tile, step, tagAgg, tagInc, hdr,
-                                      pin);
+                                      pin, wc);
+}
+
+// Statistics instance: adds this wave's look-back outcome to the workgroup's set of counters
+// (one set per XCD, by workgroup ID), one atomic per counter and wave.  `walked` lanes
+// returned a WalkCount; the others took their neighbour's inclusive value directly.
+__device__ __forceinline__ void count_walks(uint32_t* hdr, bool active, bool walked,
+                                            const WalkCount& wc) {
+    const uint64_t act = __ballot(active);
+    const uint64_t wlk = __ballot(active && walked);
+    uint32_t folded = active && walked ? wc.folded : 0u;
+    uint32_t polls = active && walked ? wc.polls : 0u;
+    uint32_t longest = active && walked ? wc.folded + 1u : 0u;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        folded += __shfl_xor(folded, m, kWave);
+        polls += __shfl_xor(polls, m, kWave);
+        const uint32_t o = __shfl_xor(longest, m, kWave);
+        longest = o > longest ? o : longest;
+    }
+    if ((threadIdx.x % kWave) == 0) {
+        uint32_t* st = hdr + kStatWordsOffset + (blockIdx.x & 7u) * kStatWords;
+        const uint32_t took = (uint32_t)__popcll(act & ~wlk), walk = (uint32_t)__popcll(wlk);
+        __hip_atomic_fetch_add(st + kStatTook, took, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(st + kStatWalked, walk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(st + kStatFolded, folded, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_max(st + kStatMaxWalk, longest, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(st + kStatPolls, polls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // Whether the tile at position `pos` along its chain (0 = the chain's first tile) publishes

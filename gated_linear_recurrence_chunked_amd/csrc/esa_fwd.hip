@@ -118,19 +118,23 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         tile_total<G, false, CQ>(sWP, sWE, ch, tp, te);
         const int64_t gl = (int64_t)cb * CB + ch;
         float carry = 0.0f;
+        constexpr bool STATS = CHAIN == kChainStats;
+        WalkCount wc{~0u, 0u};  // statistics instance: set when the lane walked back
+        bool active = false;
         if (FULL || gl < p.nLanes) {
             uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
             uint64_t* Y = p.flagY + (int64_t)tile * p.nLanes + gl;
             float pin = 1.0f;  // PROD: product of the gates of every earlier tile
             constexpr bool TEST = CHAIN == kChainTest;
-            const uint32_t det = CHAIN == kChainDefault ? 0u : p.det;
+            const uint32_t det = CHAIN == kChainDet || TEST ? p.det : 0u;
             const bool inc = det_publishes_inc(tile, det);
             if (tile == 0) {
                 carry = p.e0 ? p.e0[gl] : 0.0f;
             } else {
+                active = true;
                 carry = chain_carry<PROD, TEST ? kTestSpinLimit : kSpinLimit, CQ>(
                     p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg, tagInc, p.hdr, tp, te, &pin,
-                    det, inc);
+                    det, inc, STATS ? &wc : nullptr);
             }
             // the test instance withholds tile 0
             const bool pub = (!TEST || tile != 0) && inc;
@@ -140,6 +144,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
             }
             if (pub) publish(X, tagInc, te + Q::apply(tp, carry));
         }
+        if constexpr (STATS) count_walks(p.hdr, active, wc.folded != ~0u, wc);
         sCarry[ch] = carry;
     }
     __syncthreads();
@@ -267,6 +272,19 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
         if constexpr (std::is_same<T, _Float16>::value && DH == 64) {
             using C = FwdCfg<T, DH>;
             hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, true, false, kChainTest>),
+                               dim3(p.nCB * p.nTiles), dim3(C::NT), 0, s, p);
+            return hipGetLastError();
+        } else {
+            return hipErrorNotSupported;
+        }
+    }
+    if (p.y && p.stats) {
+        // the look-back statistics instance: fp16 and fp8 E4M3 storage with Dh = 64 (the host
+        // rejects the flag for other problems)
+        if constexpr ((std::is_same<T, _Float16>::value || std::is_same<T, f8e4m3>::value) &&
+                      DH == 64) {
+            using C = FwdCfg<T, DH>;
+            hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, true, false, kChainStats>),
                                dim3(p.nCB * p.nTiles), dim3(C::NT), 0, s, p);
             return hipGetLastError();
         } else {

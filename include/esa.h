@@ -47,6 +47,8 @@
  *   ESA_ERR_HIP          a kernel launch was rejected by the HIP runtime
  *   ESA_ERR_SCRATCH_LIMIT  (esa_scan_fwd_noalloc only) the problem needs more look-back
  *                        scratch than ESA_NOALLOC_SCRATCH_BYTES
+ *   ESA_ERR_TIMEOUT      (esa_workspace_status only) a scan on the workspace had a
+ *                        cross-tile wait time out since the workspace was last initialised
  */
 #ifndef ESA_H
 #define ESA_H
@@ -61,8 +63,9 @@ extern "C" {
 /* 1: fp32 / fp16 / bf16 storage.  2: adds the fp8 storage dtypes ESA_F8E4M3, ESA_F8E5M2,
  * the sequence-segment calls and the ESA_DETERMINISTIC mode flag.  3: adds the
  * ESA_TEST_FORCE_TIMEOUT mode flag.  4: adds esa_scan_fwd_noalloc and
- * ESA_ERR_SCRATCH_LIMIT. */
-#define ESA_ABI_VERSION 4
+ * ESA_ERR_SCRATCH_LIMIT.  5: adds esa_workspace_status, ESA_ERR_TIMEOUT and the
+ * ESA_LOOKBACK_STATS mode flag; a timed-out wait no longer makes later launches give up. */
+#define ESA_ABI_VERSION 5
 
 /* Checkpoint granularity: the forward can store the fp32 state at every 64th step. */
 #define ESA_CKPT_CHUNK 64
@@ -73,7 +76,8 @@ typedef enum {
     ESA_ERR_UNSUPPORTED = 2,
     ESA_ERR_WORKSPACE = 3,
     ESA_ERR_HIP = 4,
-    ESA_ERR_SCRATCH_LIMIT = 5
+    ESA_ERR_SCRATCH_LIMIT = 5,
+    ESA_ERR_TIMEOUT = 6
 } esa_status;
 
 /* Storage dtype of the sequence tensors (precision modes of page "Entangled State
@@ -108,11 +112,20 @@ typedef enum { ESA_DIRECT = 0, ESA_CONTROLLED = 1 } esa_mode;
  * normal use: a separate instance of the kernels runs in which the first tile of every chain
  * (first in the scan's direction) withholds its published values and the cross-tile wait
  * gives up after a few thousand polls, so every wait on a withheld value times out.  The
- * call returns normally: the workspace's abort word (see esa_workspace_init) is set, and
+ * call returns normally: the workspace records the timeout (see esa_workspace_status), and
  * every output that depends on a withheld value is NaN.  It exercises the failure path of
  * the bounded wait from the host.  Only fp16 storage with Dh = 64 has that instance
  * (ESA_ERR_UNSUPPORTED otherwise); the other calls reject the flag (ESA_ERR_INVALID_ARG). */
 #define ESA_TEST_FORCE_TIMEOUT 0x200
+
+/* Diagnostic flag OR-ed into the mode argument of esa_scan_fwd and esa_scan_bwd: a separate
+ * instance of the kernels runs that counts what the cross-tile look-back did, into the
+ * workspace header (read them with esa_workspace_status).  Results are those of the
+ * default look-back; the counting costs one set of atomics per workgroup.  fp16 and fp8 E4M3
+ * storage with Dh = 64 only (ESA_ERR_UNSUPPORTED otherwise); not combinable with
+ * ESA_DETERMINISTIC or ESA_TEST_FORCE_TIMEOUT, and rejected by the other calls
+ * (ESA_ERR_INVALID_ARG). */
+#define ESA_LOOKBACK_STATS 0x400
 
 /* ABI version of the loaded library (ESA_ABI_VERSION at build time). */
 int esa_abi_version(void);
@@ -132,11 +145,28 @@ size_t esa_scan_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dh, int
 size_t esa_scan_ckpt_bytes(int64_t B, int64_t T, int64_t H, int64_t Dh);
 
 /* Zero-fills `bytes` of workspace on `stream` (a fill kernel, safe inside graph capture).
- * Word 3 of the workspace (bytes 12..15) is a sticky abort flag: it becomes non-zero if a
- * scan's cross-tile wait ever timed out (about a second), in which case the outputs that
- * depend on the missing value are NaN.  This never happens in a correct run (it can be
- * forced with ESA_TEST_FORCE_TIMEOUT); re-initialising the workspace clears it. */
+ * This also clears the workspace's timeout record and look-back counters (see
+ * esa_workspace_status). */
 int esa_workspace_init(void *workspace, size_t bytes, void *stream);
+
+/* The state a workspace's header records, read on the host: waits for `stream`, then copies
+ * the header (a few hundred bytes; nothing is allocated).  Not callable while `stream` is
+ * being recorded into a graph (ESA_ERR_INVALID_ARG).
+ *   workspace  a scan workspace, or NULL for this device's no-allocation scratch (all zeros
+ *              before the first esa_scan_fwd_noalloc on the device)
+ *   info       uint32_t[6], out:
+ *     info[0]  0, or the tag of the last scan launch whose cross-tile wait timed out (about
+ *              a second of polling; never in a correct run, but forced by
+ *              ESA_TEST_FORCE_TIMEOUT).  That launch's outputs that depend on the missing
+ *              value are NaN; later launches are unaffected.  Cleared only by
+ *              esa_workspace_init.
+ *     info[1..5]  look-back counters of ESA_LOOKBACK_STATS launches since the last
+ *              esa_workspace_init, over the lanes of every tile but a chain's first: lanes
+ *              that found their neighbouring tile's inclusive value published; lanes that
+ *              walked back over earlier tiles' aggregates; tiles folded by those walks; the
+ *              longest walk (tiles read, the inclusive one included); unproductive polls.
+ * Returns ESA_ERR_TIMEOUT when info[0] is non-zero, ESA_OK otherwise. */
+int esa_workspace_status(const void *workspace, uint32_t *info, void *stream);
 
 /* Forward scan with fused gate and readout: prefill and training forward (page "Entangled
  * State Attention", "[ ARCHITECTURE ]": associative composition over the sequence, then a

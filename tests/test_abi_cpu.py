@@ -16,7 +16,7 @@ from gated_linear_recurrence_chunked_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "esa.h")
 
-OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+OK, INVALID, UNSUPPORTED, WORKSPACE, SCRATCH_LIMIT = 0, 1, 2, 3, 5
 
 
 def declared_functions():
@@ -47,11 +47,12 @@ def header_abi_version() -> int:
 
 
 def test_version_and_status_strings(lib):
-    assert lib.esa_abi_version() == header_abi_version() == 4
-    for s in range(5):
-        assert lib.esa_status_string(s).decode().startswith(
-            ["ESA_OK", "ESA_ERR_INVALID_ARG", "ESA_ERR_UNSUPPORTED", "ESA_ERR_WORKSPACE",
-             "ESA_ERR_HIP"][s])
+    assert lib.esa_abi_version() == header_abi_version() == 5
+    names = ["ESA_OK", "ESA_ERR_INVALID_ARG", "ESA_ERR_UNSUPPORTED", "ESA_ERR_WORKSPACE",
+             "ESA_ERR_HIP", "ESA_ERR_SCRATCH_LIMIT", "ESA_ERR_TIMEOUT"]
+    for s, name in enumerate(names):
+        assert lib.esa_status_string(s).decode().startswith(name)
+        assert binding.STATUS_NAMES[s] == name
     assert lib.esa_status_string(99)
 
 
@@ -101,7 +102,7 @@ def test_fwd_validation(lib):
     assert fwd(lib, T=-1) == INVALID
     assert fwd(lib, dt=5) == INVALID
     assert fwd(lib, mode=0x102) == INVALID  # deterministic flag with a bad form
-    assert fwd(lib, mode=0x400) == INVALID  # unknown flag
+    assert fwd(lib, mode=0x800) == INVALID  # unknown flag
     assert fwd(lib, mode=0x202) == INVALID  # test flag with a bad form
     assert fwd(lib, Dh=64, mode=0x301, y=1) == INVALID  # both flags: the rest still validates
     assert fwd(lib, mode=0x101, y=1) == INVALID  # a valid flagged mode still validates the rest
@@ -235,3 +236,49 @@ def test_torch_call_path_loads():
     for name in ("scan_fwd", "scan_bwd", "state_step", "segment_fwd", "segment_bwd",
                  "segment_compose"):
         assert callable(getattr(_esa_torch, name))
+
+
+def test_stats_flag_validation(lib):
+    """ESA_LOOKBACK_STATS (0x400) is accepted by esa_scan_fwd and esa_scan_bwd for fp16 and
+    fp8 E4M3 storage with Dh = 64, alone; every check returns before any launch (a valid
+    flagged call here stops at the zero-byte workspace)."""
+    S = 0x400
+    assert fwd(lib, dt=1, Dh=64, mode=1 | S) == WORKSPACE
+    assert fwd(lib, dt=3, Dh=64, mode=0 | S) == WORKSPACE
+    for dt in (0, 2, 4):
+        assert fwd(lib, dt=dt, Dh=64, mode=1 | S) == UNSUPPORTED
+    assert fwd(lib, dt=1, Dh=32, mode=1 | S) == UNSUPPORTED
+    assert fwd(lib, dt=1, Dh=64, mode=1 | S | 0x100) == INVALID
+    assert fwd(lib, dt=1, Dh=64, mode=1 | S | 0x200) == INVALID
+    p = [addr(k) for k in range(1, 6)]
+    assert lib.esa_state_step(4, 2, 64, 1, 1 | S, *p, None) == INVALID
+    assert lib.esa_scan_segment_fwd(2, 100, 2, 64, 1, 1 | S, addr(1), addr(2), addr(3), addr(4),
+                                    addr(5), 0, None) == INVALID
+
+
+def test_workspace_status_validation(lib):
+    info = (ctypes.c_uint32 * 6)()
+    assert lib.esa_workspace_status(addr(1), None, None) == INVALID
+    assert lib.esa_workspace_status(ctypes.c_void_p(0x100000008), info, None) == INVALID
+
+
+def test_noalloc_validation(lib):
+    """esa_scan_fwd_noalloc refuses, before any HIP call, a problem whose look-back words
+    exceed its static array, the forced-timeout flag, and what esa_scan_fwd refuses."""
+    def big(k):  # fake device addresses 8 GiB apart (the sequences here are 2 GiB)
+        return ctypes.c_void_p(0x1000000000 + k * (1 << 33))
+
+    def na(B=256, T=8192, H=8, Dh=64, dt=1, mode=1, a=1, y=4, eT=5):
+        pa = None if a is None else big(a)
+        py = None if y is None else big(y)
+        pe = None if eT is None else big(eT)
+        return lib.esa_scan_fwd_noalloc(B, T, H, Dh, dt, mode, pa, big(2), big(3), None, py,
+                                        pe, None, None)
+
+    assert na() == SCRATCH_LIMIT  # 64 MiB + 256 B of look-back words
+    assert lib.esa_status_string(SCRATCH_LIMIT).decode().startswith("ESA_ERR_SCRATCH_LIMIT")
+    assert na(T=100, mode=1 | 0x200) == INVALID
+    assert na(a=None) == INVALID
+    assert na(y=2) == INVALID
+    assert na(Dh=48) == UNSUPPORTED
+    assert na(T=0, a=None, y=None, eT=None) == OK  # nothing to launch

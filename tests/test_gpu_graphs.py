@@ -96,3 +96,54 @@ def test_recorded_scans_replay_correctly(dt, mode, det):
     for ws in binding._workspaces.values():
         assert int(ws[12:16].view(torch.int32).item()) == 0, "look-back wait timed out"
     del g
+
+
+def test_replay_after_the_stream_workspace_grew():
+    """A recorded scan keeps the raw address of the workspace it ran on.  An eager call on
+    the capture stream that needs more workspace makes the binding cache a larger one; the
+    superseded workspace must stay alive, since every replay still writes its look-back words
+    there.  Memory allocated after the growth (where a freed workspace would be reused) keeps
+    its contents through the replays, and every replay matches the oracle."""
+    dt, mode = torch.float16, "controlled"
+    B, T, H, Dh = 2, 2000, 2, 64
+    say("graph replay after the workspace grew")
+    shp = (B, T, H, Dh)
+    x = {k: synth.normal(shp, 4500 + i, 0.5 if k == "a" else 0.0, 1.0, dt).to(DEV)
+         for i, k in enumerate(("a", "v", "q", "dy"))}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        binding.scan_fwd(x["a"], x["v"], x["q"], mode=mode, return_ckpt=True)
+        ws_before = binding.get_workspace(0, DEV)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        y, eT, ck = binding.scan_fwd(x["a"], x["v"], x["q"], mode=mode, return_ckpt=True)
+        da, dv, dq, _ = binding.scan_bwd(x["a"], x["v"], x["q"], x["dy"], ckpt=ck, mode=mode)
+    c = {k: t.cpu() for k, t in x.items()}
+    ry, _ = oracle.scan_fwd(c["a"], c["v"], c["q"], mode=1, threads=8)
+    rda, rdv, rdq, _ = oracle.scan_bwd(c["a"], c["v"], c["q"], c["dy"], mode=1, threads=8)
+    # a problem 16 times larger, eagerly on the capture stream: the cached workspace grows
+    big = {k: synth.normal((B, 16 * T, H, Dh), 4600 + i, 0.0, 1.0, dt).to(DEV)
+           for i, k in enumerate("avq")}
+    with torch.cuda.stream(s):
+        binding.scan_fwd(big["a"], big["v"], big["q"], mode=mode)
+        ws_after = binding.get_workspace(0, DEV)
+    torch.cuda.synchronize()
+    assert ws_after.data_ptr() != ws_before.data_ptr()
+    nb = ws_before.numel()
+    del ws_before
+    junk = torch.full((nb,), 0x5A, dtype=torch.uint8, device=DEV)
+    for r in range(3):
+        with torch.cuda.stream(s):
+            g.replay()
+            binding.scan_fwd(big["a"], big["v"], big["q"], mode=mode)  # eager, between replays
+        torch.cuda.synchronize()
+        say(f"  replay {r}")
+        assert bool((junk == 0x5A).all()), "a replay wrote into memory it does not own"
+        assert_close(f"y replay {r}", y, ry, dt)
+        assert_close(f"d_logit replay {r}", da, rda, dt)
+        assert_close(f"d_value replay {r}", dv, rdv, dt)
+        assert_close(f"d_query replay {r}", dq, rdq, dt)
+    del g
