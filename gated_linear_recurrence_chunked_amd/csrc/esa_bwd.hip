@@ -30,7 +30,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, HL = G::HL;
     constexpr int TT = G::TT;
     constexpr int ES = sizeof(T);
-    constexpr bool CQ = sizeof(T) == 4;  // fp32 storage carries gate products as complements
+    constexpr bool CQ = true;  // gate products are carried as complements (GP)
     using Q = GP<CQ>;
     const uint32_t epoch = launch_epoch(p.epoch, p.epochWord);
     const uint32_t tagAgg = make_tag(epoch, kTagAgg);
@@ -102,9 +102,10 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     }
 
     // ---- gates and the thread's forward fold ----
-    // S_[i][e] = s (or 1 - s with complements); U_[i][e] = 1 - s (controlled, products) or
-    // s (1 - s); V_[i][e] = v
-    float S_[L][VEC], U_[L][VEC], V_[L][VEC];
+    // S_[i][e] = 1 - s (the complement, GP); V_[i][e] = v (masked steps: 0 and 0, the
+    // identity); with fp32 storage also U_[i][e] = s (1 - s) (gate_u_slope)
+    constexpr bool SLOPE = sizeof(T) == 4;
+    float S_[L][VEC], V_[L][VEC], U_[SLOPE ? L : 1][VEC];
     float P[VEC], E[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -119,15 +120,18 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         unpack<T>(rv[i], V_[i]);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            float s, u;
-            gate<T>(av[e], s, u);
-            s = ok ? s : 1.0f;
-            u = ok ? u : 0.0f;
-            S_[i][e] = CQ ? u : s;
-            U_[i][e] = MODE == kDirect || CQ ? s * u : u;
-            const float bt = MODE == kDirect ? (ok ? V_[i][e] : 0.0f) : u * V_[i][e];
-            E[e] = Q::apply(S_[i][e], E[e]) + bt;
-            P[e] = Q::mul(P[e], S_[i][e]);
+            float u;
+            if constexpr (SLOPE) {
+                float su;
+                u = gate_u_slope(av[e], su);
+                U_[i][e] = ok ? su : 0.0f;
+            } else {
+                u = gate_u(av[e]);
+            }
+            S_[i][e] = ok ? u : 0.0f;
+            V_[i][e] = ok ? V_[i][e] : 0.0f;
+            E[e] = update<MODE>(E[e], S_[i][e], V_[i][e]);
+            P[e] = i == 0 ? S_[i][e] : Q::mul(P[e], S_[i][e]);
         }
     }
 
@@ -154,9 +158,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             Eprev[e] = E[e];
-            const float uc = CQ ? S_[i][e] : U_[i][e];  // 1 - s
-            const float bt = MODE == kDirect ? (ok ? V_[i][e] : 0.0f) : uc * V_[i][e];
-            E[e] = Q::apply(S_[i][e], E[e]) + bt;
+            E[e] = update<MODE>(E[e], S_[i][e], V_[i][e]);
             ss += E[e] * E[e];
         }
         ss = head_sum<HL>(ss);
@@ -178,7 +180,9 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         for (int e = 0; e < VEC; ++e) {
             Gr[i][e] = ok ? r * (dn[e] - n[e] * mu) : 0.0f;
             // gate factor w, stored over V_: d_logit = dE * w
-            const float su = MODE == kDirect || CQ ? U_[i][e] : S_[i][e] * U_[i][e];
+            float su;  // s (1 - s)
+            if constexpr (SLOPE) su = U_[i][e];
+            else su = gate_slope(S_[i][e]);
             V_[i][e] = MODE == kDirect ? Eprev[e] * su : (Eprev[e] - V_[i][e]) * su;
         }
         if constexpr (GRADS) {
@@ -196,7 +200,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
 #pragma unroll
         for (int i = L - 1; i >= 0; --i) {
             er = Q::apply(S_[i][e], Gr[i][e] + er);
-            pr = Q::mul(S_[i][e], pr);
+            pr = i == L - 1 ? S_[i][e] : Q::mul(S_[i][e], pr);
         }
         P[e] = pr;
         E[e] = er;
@@ -255,7 +259,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
             const float dE = Gr[i][e] + lam[e];
             lam[e] = Q::apply(S_[i][e], dE);
             dav[e] = dE * V_[i][e];
-            dvv[e] = MODE == kDirect ? dE : dE * (CQ ? S_[i][e] : U_[i][e]);
+            dvv[e] = MODE == kDirect ? dE : dE * S_[i][e];
         }
         if constexpr (GRADS) {
             if constexpr (FULL) {

@@ -436,26 +436,39 @@ __device__ __forceinline__ void st16(void* base, int64_t elem_off, int esize, co
         *reinterpret_cast<uint2*>(p) = make_uint2(v.x, v.y);
 }
 
-// Gate: s = sigma(a) = 1 / (1 + exp(-a)) and u = 1 - s = sigma(-a), taken as exp(-a) * s so
-// that it keeps full relative precision when s is close to 1.  exp(-a) is capped at 2^126 so
-// that 1 + exp(-a) stays finite (for a < -87 the true s is below 2^-126 and 2^-126 is used);
-// a NaN logit stays NaN.
-//
-// With fp32 storage (the tightest parity bar) s itself is taken as 1 - u when a > 0: u is
-// relatively exact, so 1 - u is s correctly rounded, whereas 1 / (1 + e) carries the rounding
-// of 1 + e and of the reciprocal (measured: off by one unit in the last place in half the
-// cases, with a bias).  A retentive chain (1 - s ~ 1e-4) sums that bias over its ~1 / (1 - s)
-// steps of memory: at a ~ N(6, 1) over 15000 steps the largest error (in the gate gradient)
-// drops from 8.8e-5 to 1.5e-5 and that of y from 1.4e-5 to 5.4e-6.  The extra instructions are skipped for 16- and 8-bit storage, whose bars are
-// orders of magnitude wider than this error.
-template <typename T>
-__device__ __forceinline__ void gate(float a, float& s, float& u) {
-    float x = a * -1.4426950408889634f;  // -a * log2(e)
-    x = x > 126.0f ? 126.0f : x;
-    const float e = __builtin_amdgcn_exp2f(x);
-    s = __builtin_amdgcn_rcpf(1.0f + e);
-    u = e * s;
-    if constexpr (sizeof(T) == 4) s = a > 0.0f ? 1.0f - u : s;
+// Gate complement: u = 1 - s = sigma(-a) = 1 / (1 + exp(a)), for s = sigma(a).  The kernels
+// carry gates only as complements (see GP and update()), so s itself is never formed.  u
+// keeps its full relative precision where s is close to 1 (long memory), which 1 - s computed
+// by subtraction would lose.  No clamp is needed: for a above about 88, exp(a) is +inf and u
+// is 0 (s = 1); for a below about -104, exp(a) is 0 and u is 1 (s = 0); a NaN logit gives NaN.
+// The backward's gate derivative s (1 - s) = u - u^2 is taken from u with one fma: exact
+// relative to u, and within one unit in the last place of u absolutely (so relatively coarse
+// only where s itself is tiny, where the derivative is small against its neighbours; the
+// 16- and 8-bit bars are far wider than that error, fp32 storage uses gate_u_slope).
+__device__ __forceinline__ float gate_u(float a) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * 1.4426950408889634f));
+}
+__device__ __forceinline__ float gate_slope(float u) { return __builtin_fmaf(-u, u, u); }
+// The same complement with the derivative s (1 - s) = exp(a) u^2 to full relative precision,
+// for fp32 storage, whose bar would see the absolute error of u - u^2 where s is small.
+// exp(a) is capped at 2^126 so that s (1 - s) is 0, not NaN, where it overflows (u is 0
+// there).
+__device__ __forceinline__ float gate_u_slope(float a, float& slope) {
+    const float e = __builtin_amdgcn_exp2f(a * 1.4426950408889634f);
+    const float u = __builtin_amdgcn_rcpf(1.0f + e);
+    slope = __builtin_fminf(e, 0x1p126f) * u * u;
+    return u;
+}
+
+// One step of the recurrence on the state x with the gate's complement u (see GP):
+//   controlled  x + u (v - x) = s x + (1 - s) v
+//   direct      x - u x + v   = s x + v
+// Both keep x's relative precision when u is small (long memory).  A masked step passes
+// u = 0 and v = 0, which leaves x unchanged.
+template <int MODE>
+__device__ __forceinline__ float update(float x, float u, float v) {
+    if constexpr (MODE == kControlled) return __builtin_fmaf(u, v - x, x);
+    else return __builtin_fmaf(-u, x, x) + v;
 }
 
 // Sum over the HL consecutive, aligned threads that hold one head; every thread of the head
@@ -477,16 +490,16 @@ __device__ __forceinline__ float head_sum(float x) {
     return x;
 }
 
-// Gate products of a pair, in one of two representations.  GP<false> carries the product P
-// itself.  GP<true> carries its complement q = 1 - P, for fp32 storage: there the gates of a
-// retentive lane lie within 1e-4 of 1, and the fp32 product of two such factors drops its
-// second-order term (below half a unit in the last place next to 1), always in the same
-// direction; the cross-tile carry c <- e + P c divides that bias by 1 - P, so the state drifts
-// along the sequence.  The complement of a product, q1 + q2 - q1 q2, keeps its relative
-// precision, and (1 - q) x = x - q x loses nothing next to 1.  Where P is small instead, the
-// complement leaves an absolute error of about one unit in the last place of x in (1 - q) x,
-// i.e. relative to the state being decayed, which the parity metric's scale already covers.
-// The 16-bit and 8-bit storages keep GP<false>: their bars are 500x wider than that drift.
+// Gate products of a pair, in one of two representations.  GP<true>, used by every scan, carries
+// the complement q = 1 - P of a product P of gates: along a long-memory lane the gates lie
+// within 1e-4 of 1, and an fp32 product of two such factors drops its second-order term
+// (below half a unit in the last place next to 1), always in the same direction; the
+// cross-tile carry c <- e + P c divides that bias by 1 - P, so the state would drift along
+// the sequence.  The complement of a product, q1 + q2 - q1 q2, keeps its relative precision,
+// and (1 - q) x = x - q x loses nothing next to 1.  Where P is small instead, the complement
+// leaves an absolute error of about one unit in the last place of x in (1 - q) x, i.e.
+// relative to the state being decayed, which the parity metric's scale already covers.
+// GP<false> carries the product itself: the plain form of the same interface.
 template <bool CQ>
 struct GP;
 template <>
@@ -641,8 +654,9 @@ __device__ __forceinline__ float word_val(uint64_t w) {
 // hanging.  A correct run never comes near the limit (about a second of polling).
 //
 // With PROD (sequence-segment aggregates) a tile's inclusive word in flagY holds the product
-// of every gate from the chain's start through that tile; *pinc then receives the product
-// through the tile before `tile` (NaN when the wait gave up).
+// of every gate from the chain's start through that tile (in GP<CQ>'s representation);
+// *pinc then receives the product through the tile before `tile` (NaN when the wait gave
+// up).
 constexpr uint32_t kSpinLimit = 1u << 20;
 // The forced-timeout test instances (a separate kernel instantiation, so the normal kernels
 // carry no trace of it): the chain's first tile withholds its publications and every wait
@@ -680,7 +694,6 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
                                            int64_t nLanes, int64_t lane, int64_t tile, int step,
                                            uint32_t tagAgg, uint32_t tagInc, uint32_t* hdr,
                                            float* pinc = nullptr, WalkCount* wc = nullptr) {
-    static_assert(!(PROD && CQ), "the gate product of a segment is carried as itself");
     float ap = GP<CQ>::one, ae = 0.0f;
     int64_t j = tile + step;
     uint32_t polls = 0;
@@ -697,8 +710,8 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
             // the inclusive product is published beside the inclusive state, in no fixed
             // order: wait until it is visible too
             if (word_tag(yv) == tagInc) {
-                *pinc = ap * word_val(yv);
-                return ae + ap * word_val(x);
+                *pinc = GP<CQ>::mul(ap, word_val(yv));
+                return ae + GP<CQ>::apply(ap, word_val(x));
             }
         }
         if (tg == tagAgg && word_tag(yv) == tagAgg) {

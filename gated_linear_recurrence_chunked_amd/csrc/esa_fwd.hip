@@ -25,9 +25,9 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
     constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, HL = G::HL;
     constexpr int TT = G::TT;
     constexpr int ES = sizeof(T);
-    // fp32 storage carries gate products as complements (GP); the segment pass's gate
-    // product output stays a product
-    constexpr bool CQ = sizeof(T) == 4 && !PROD;
+    // gate products are carried as complements (GP); the segment pass converts its gate
+    // product output back to a product at the end
+    constexpr bool CQ = true;
     using Q = GP<CQ>;
     static_assert(kCkptChunk % L == 0, "checkpoint steps must end a thread's slot");
     const uint32_t epoch = launch_epoch(p.epoch, p.epochWord);
@@ -78,8 +78,9 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         }
     }
 
-    // ---- level 1: gates and the thread's own fold (identity pair where masked) ----
-    float A[L][VEC], Bt[L][VEC];
+    // ---- level 1: gates and the thread's own fold (identity step where masked) ----
+    // U: the gate's complement 1 - s; V: the value (both 0 on a masked step)
+    float U[L][VEC], V[L][VEC];
     float P[VEC], E[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -94,13 +95,11 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         unpack<T>(rv[i], vv);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            float s, u;
-            gate<T>(av[e], s, u);
-            const float bt = MODE == kDirect ? vv[e] : u * vv[e];
-            A[i][e] = ok ? (CQ ? u : s) : Q::one;  // the gate, or its complement
-            Bt[i][e] = ok ? bt : 0.0f;
-            E[e] = Q::apply(A[i][e], E[e]) + Bt[i][e];
-            P[e] = Q::mul(P[e], A[i][e]);
+            const float u = gate_u(av[e]);
+            U[i][e] = ok ? u : 0.0f;
+            V[i][e] = ok ? vv[e] : 0.0f;
+            E[e] = update<MODE>(E[e], U[i][e], V[i][e]);
+            P[e] = i == 0 ? U[i][e] : Q::mul(P[e], U[i][e]);
         }
     }
 
@@ -124,7 +123,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         if (FULL || gl < p.nLanes) {
             uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
             uint64_t* Y = p.flagY + (int64_t)tile * p.nLanes + gl;
-            float pin = 1.0f;  // PROD: product of the gates of every earlier tile
+            float pin = Q::one;  // PROD: product of the gates of every earlier tile
             constexpr bool TEST = CHAIN == kChainTest;
             const uint32_t det = CHAIN == kChainDet || TEST ? p.det : 0u;
             const bool inc = det_publishes_inc(tile, det);
@@ -139,8 +138,9 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
             // the test instance withholds tile 0
             const bool pub = (!TEST || tile != 0) && inc;
             if constexpr (PROD) {
-                if (pub) publish(Y, tagInc, tp * pin);
-                if (tile == p.nTiles - 1) p.prod[gl] = tp * pin;
+                const float prod = Q::mul(tp, pin);
+                if (pub) publish(Y, tagInc, prod);
+                if (tile == p.nTiles - 1) p.prod[gl] = CQ ? 1.0f - prod : prod;
             }
             if (pub) publish(X, tagInc, te + Q::apply(tp, carry));
         }
@@ -193,7 +193,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         float ss = 0.0f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            E[e] = Q::apply(A[i][e], E[e]) + Bt[i][e];
+            E[e] = update<MODE>(E[e], U[i][e], V[i][e]);
             ss += E[e] * E[e];
         }
         if constexpr (READOUT) {

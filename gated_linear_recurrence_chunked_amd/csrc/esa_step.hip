@@ -1,5 +1,6 @@
 // One-token recurrent update with readout, for generation, on gfx950: per lane
-// E <- s E + B (B = v direct, (1 - s) v controlled), then y = q E / sqrt(mean_h E^2 + eps).
+// E <- s E + B (B = v direct, (1 - s) v controlled), evaluated as the scans' step (update()),
+// then y = q E / sqrt(mean_h E^2 + eps).
 // Page "Entangled State Attention", section "[ ARCHITECTURE ]" (one-token update reusing the
 // state) and "[ QUICK START ]" (decode_step); page "Entangled State Attention v2.1",
 // section 5 (lightning_step).  The fp32 state is updated in place.
@@ -42,9 +43,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     float ss = 0.0f;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-        float s, u;
-        gate<T>(av[e], s, u);
-        st[e] = s * st[e] + (MODE == kDirect ? vv[e] : u * vv[e]);
+        st[e] = update<MODE>(st[e], gate_u(av[e]), vv[e]);
         ss += st[e] * st[e];
     }
     ss = head_sum<HL>(ss);

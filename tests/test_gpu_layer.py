@@ -66,11 +66,11 @@ def test_scan_autograd(dt, mode):
     ry, reT = oracle.scan_fwd(x["a"], x["v"], x["q"], e0, mode=MODES[mode])
     rda, rdv, rdq, rde0 = oracle.scan_bwd(x["a"], x["v"], x["q"], w, e0, u, mode=MODES[mode])
     assert_close("y", y, ry, dt)
-    assert_close("eT", eT, reT, dt)
+    assert_close("eT", eT, reT, torch.float32)
     assert_close("d_logit", g["a"].grad, rda, dt)
     assert_close("d_value", g["v"].grad, rdv, dt)
     assert_close("d_query", g["q"].grad, rdq, dt)
-    assert_close("d_init", ge0.grad, rde0, dt)
+    assert_close("d_init", ge0.grad, rde0, torch.float32)
 
 
 def reference_layer(layer, x, mode, e0=None, storage=None):
@@ -164,7 +164,7 @@ def test_layer_with_fp8_scan_storage(scan_dtype):
         r, rst = oracle.scan_fwd(a, v, q, mode=1)
         ry = torch.from_numpy(r).to(scan_dtype).double().reshape(B, T, C) @ layer.W_O.double().cpu()
     assert_close("y", y, ry, scan_dtype)
-    assert_close("state", st, rst, torch.float16)
+    assert_close("state", st, rst, torch.float32)
 
 
 def test_layer_with_state_dim_different_from_embd():

@@ -53,7 +53,7 @@ def test_stats_instance_counts_every_lane(dt):
     ry, reT = oracle.scan_fwd(x["a"], x["v"], x["q"], mode=1, threads=8)
     rda, rdv, rdq, rde0 = oracle.scan_bwd(x["a"], x["v"], x["q"], x["dy"], mode=1, threads=8)
     assert_close("y", y, ry, dt)
-    assert_close("final_state", eT, reT, torch.float16)
+    assert_close("final_state", eT, reT, torch.float32)
     assert_close("d_logit", da, rda, dt)
     assert_close("d_value", dv, rdv, dt)
     assert_close("d_query", dq, rdq, dt)

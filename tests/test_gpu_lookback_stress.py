@@ -55,13 +55,13 @@ def test_long_single_chain(gate, dt, mode):
     ry, reT = oracle.scan_fwd(a, v, q, e0, mode=m)
     r = oracle.scan_bwd(a, v, q, dy, e0, None, mode=m)
     assert_close("y", y, ry, dt)
-    assert_close("eT", eT, reT, dt)
+    assert_close("eT", eT, reT, torch.float32)
     for name, got, ref in zip(("d_logit", "d_value", "d_query", "d_init"), (da, dv, dq, de0), r):
         # a saturated gate makes some outputs numerically zero (s (1 - s), and 1 - s or s
         # itself, are 0 or ~1e-38 in fp32 but ~1e-44 in fp64): those are compared absolutely at
         # the 1e-30 level; outputs of normal size are unaffected by the floor
         floor = 1e-30 if gate != "random" else 0.0
-        assert_close(name, got, ref, dt, floor=floor)
+        assert_close(name, got, ref, torch.float32 if name == "d_init" else dt, floor=floor)
 
 
 @pytest.mark.parametrize("dt,mode", [(torch.float8_e4m3fn, "controlled"),
@@ -87,9 +87,9 @@ def test_long_single_chain_fp8(dt, mode):
     ry, reT = oracle.scan_fwd(a, v, q, e0, mode=m)
     r = oracle.scan_bwd(a, v, q, dy, e0, None, mode=m)
     assert_close("y", y, ry, dt)
-    assert_close("eT", eT, reT, torch.float16)
+    assert_close("eT", eT, reT, torch.float32)
     for name, got, ref in zip(("d_logit", "d_value", "d_query", "d_init"), (da, dv, dq, de0), r):
-        assert_close(name, got, ref, torch.float16 if name == "d_init" else dt)
+        assert_close(name, got, ref, torch.float32 if name == "d_init" else dt)
 
 
 def test_repeated_runs_agree():
@@ -158,12 +158,12 @@ def test_deterministic_flag_gives_bitwise_identical_runs(dt, mode, B, T, H, Dh, 
     rda, rdv, rdq, rde0 = oracle.scan_bwd(x["a"], x["v"], x["q"], x["dy"], e0, None, mode=m)
     y, eT, _, da, dv, dq, de0, _, _, da2, dv2, dq2, de02 = runs[0]
     assert_close("y", y, ry, dt)
-    assert_close("eT", eT, reT, dt)
+    assert_close("eT", eT, reT, torch.float32)
     for name, got, ref in (("d_logit", da, rda), ("d_value", dv, rdv), ("d_query", dq, rdq),
                            ("d_init", de0, rde0), ("d_logit (no ckpt)", da2, rda),
                            ("d_value (no ckpt)", dv2, rdv), ("d_query (no ckpt)", dq2, rdq),
                            ("d_init (no ckpt)", de02, rde0)):
-        assert_close(name, got, ref, dt)
+        assert_close(name, got, ref, torch.float32 if name.startswith("d_init") else dt)
 
 
 def test_concurrent_streams_with_their_own_workspaces():
@@ -208,4 +208,4 @@ def test_concurrent_streams_with_their_own_workspaces():
     c = {k: t.cpu() for k, t in probs[1].items()}
     ry, reT = oracle.scan_fwd(c["a"], c["v"], c["q"], c["e0"], mode=1)
     assert_close("y", got[1][0], ry, dt)
-    assert_close("eT", got[1][1], reT, dt)
+    assert_close("eT", got[1][1], reT, torch.float32)
