@@ -24,14 +24,16 @@
 namespace esa {
 
 template <typename T, int MODE, int DH, int L, int NT, bool GRADS, bool FULL, int CHAIN>
-__device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint32_t cb, float* sP,
-                                         float* sE, float* sWP, float* sWE, float* sCarry) {
+__device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint32_t cb,
+                                         Acc<T>* sP, Acc<T>* sE, Acc<T>* sWP, Acc<T>* sWE,
+                                         Acc<T>* sCarry) {
     using G = Geom<T, DH, L, NT>;
     constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, HL = G::HL;
     constexpr int TT = G::TT;
     constexpr int ES = sizeof(T);
     constexpr bool CQ = true;  // gate products are carried as complements (GP)
-    using Q = GP<CQ>;
+    using F = Acc<T>;          // the accumulation type (Acc)
+    using Q = GP<CQ, F>;
     const uint32_t epoch = launch_epoch(p.epoch, p.epochWord);
     const uint32_t tagAgg = make_tag(epoch, kTagAgg);
     const uint32_t tagInc = make_tag(epoch, kTagInc);
@@ -106,11 +108,11 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     // identity); with fp32 storage also U_[i][e] = s (1 - s) (gate_u_slope)
     constexpr bool SLOPE = sizeof(T) == 4;
     float S_[L][VEC], V_[L][VEC], U_[SLOPE ? L : 1][VEC];
-    float P[VEC], E[VEC];
+    F P[VEC], E[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
         P[e] = Q::one;
-        E[e] = 0.0f;
+        E[e] = F(0);
     }
 #pragma unroll
     for (int i = 0; i < L; ++i) {
@@ -130,36 +132,37 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
             }
             S_[i][e] = ok ? u : 0.0f;
             V_[i][e] = ok ? V_[i][e] : 0.0f;
-            E[e] = update<MODE>(E[e], S_[i][e], V_[i][e]);
-            P[e] = i == 0 ? S_[i][e] : Q::mul(P[e], S_[i][e]);
+            E[e] = update<MODE, F>(E[e], F(S_[i][e]), F(V_[i][e]));
+            P[e] = i == 0 ? F(S_[i][e]) : Q::mul(P[e], F(S_[i][e]));
         }
     }
 
     // ---- state entering this thread's steps: the checkpoint at the tile start, carried
     //      through the earlier slots of the tile (two-phase slot scan, no look-back needed) ----
     const int w = tid / kWave;
-    float xp[G::CPL][G::SPW], xe[G::CPL][G::SPW];
-    float XP[VEC], XE[VEC];
-    slots_phase_a<G, false, CQ>(P, E, sP, sE, sWP, sWE, xp, xe);
+    F xp[G::CPL][G::SPW], xe[G::CPL][G::SPW];
+    F XP[VEC], XE[VEC];
+    slots_phase_a<G, false, CQ, F>(P, E, sP, sE, sWP, sWE, xp, xe);
     __syncthreads();
-    slots_phase_b<G, false, CQ>(sP, sE, sWP, sWE, xp, xe);
+    slots_phase_b<G, false, CQ, F>(sP, sE, sWP, sWE, xp, xe);
     __syncthreads();
     read_exclusive<G>(sP, sE, XP, XE);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) E[e] = XE[e] + Q::apply(XP[e], cin[e]);
+    for (int e = 0; e < VEC; ++e) E[e] = XE[e] + Q::apply(XP[e], F(cin[e]));
 
     // ---- re-run the forward per step; readout backward; keep gE and the gate factor ----
     float Gr[L][VEC];
 #pragma unroll
     for (int i = 0; i < L; ++i) {
         const bool ok = FULL || (lane_ok && t0 + i < p.T);
-        float Eprev[VEC];
-        float ss = 0.0f;
+        F Eprev[VEC];
+        float ss = 0.0f, Ef[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             Eprev[e] = E[e];
-            E[e] = update<MODE>(E[e], S_[i][e], V_[i][e]);
-            ss += E[e] * E[e];
+            E[e] = update<MODE, F>(E[e], F(S_[i][e]), F(V_[i][e]));
+            Ef[e] = float(E[e]);
+            ss += Ef[e] * Ef[e];
         }
         ss = head_sum<HL>(ss);
         const float r = __builtin_amdgcn_rsqf(ss * (1.0f / DH) + kEps);
@@ -169,7 +172,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         float dd = 0.0f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            n[e] = E[e] * r;
+            n[e] = Ef[e] * r;
             dqv[e] = dyv[e] * n[e];
             dn[e] = dyv[e] * qv[e];
             dd += dn[e] * n[e];
@@ -183,7 +186,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
             float su;  // s (1 - s)
             if constexpr (SLOPE) su = U_[i][e];
             else su = gate_slope(S_[i][e]);
-            V_[i][e] = MODE == kDirect ? Eprev[e] * su : (Eprev[e] - V_[i][e]) * su;
+            V_[i][e] = float(MODE == kDirect ? Eprev[e] * F(su) : (Eprev[e] - F(V_[i][e])) * F(su));
         }
         if constexpr (GRADS) {
             if constexpr (FULL)
@@ -196,28 +199,28 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     // ---- reverse fold of the thread's steps: lam_out = P * lam_in + E ----
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-        float pr = Q::one, er = 0.0f;
+        F pr = Q::one, er = F(0);
 #pragma unroll
         for (int i = L - 1; i >= 0; --i) {
-            er = Q::apply(S_[i][e], Gr[i][e] + er);
-            pr = i == L - 1 ? S_[i][e] : Q::mul(S_[i][e], pr);
+            er = Q::apply(F(S_[i][e]), F(Gr[i][e]) + er);
+            pr = i == L - 1 ? F(S_[i][e]) : Q::mul(F(S_[i][e]), pr);
         }
         P[e] = pr;
         E[e] = er;
     }
     // the slot arrays are reused: this thread's slot positions were last read by this thread,
     // and the wave aggregates by every wave before the barrier above
-    slots_phase_a<G, true, CQ>(P, E, sP, sE, sWP, sWE, xp, xe);
+    slots_phase_a<G, true, CQ, F>(P, E, sP, sE, sWP, sWE, xp, xe);
     __syncthreads();
-    slots_phase_b<G, true, CQ>(sP, sE, sWP, sWE, xp, xe);
+    slots_phase_b<G, true, CQ, F>(sP, sE, sWP, sWE, xp, xe);
 
     // ---- reverse look-back across tiles, wave k for channels 64k.. (lane = channel) ----
     if (w < G::CPL) {
         const int ch = (tid % kWave) + w * kWave;
-        float tp, te;
-        tile_total<G, true, CQ>(sWP, sWE, ch, tp, te);
+        F tp, te;
+        tile_total<G, true, CQ, F>(sWP, sWE, ch, tp, te);
         const int64_t gl = (int64_t)cb * CB + ch;
-        float carry = 0.0f;
+        F carry = F(0);
         constexpr bool STATS = CHAIN == kChainStats;
         WalkCount wc{~0u, 0u};  // statistics instance: set when the lane walked back
         bool active = false;
@@ -231,11 +234,11 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
             } else {
                 float pin;  // unused: the backward carries no gate product
                 active = true;
-                carry = chain_carry<false, TEST ? kTestSpinLimit : kSpinLimit, CQ>(
-                    p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc, p.hdr, tp, te, &pin,
-                    det, inc, STATS ? &wc : nullptr);
+                carry = chain_carry<false, TEST ? kTestSpinLimit : kSpinLimit, CQ, F>(
+                    p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc, p.hdr, float(tp),
+                    float(te), &pin, det, inc, STATS ? &wc : nullptr);
             }
-            const float lam_out = te + Q::apply(tp, carry);
+            const float lam_out = float(te + Q::apply(tp, F(carry)));
             // the test instance withholds the last tile
             if ((!TEST || tile != p.nTiles - 1) && inc) publish(X, tagInc, lam_out);
             if (tile == 0 && p.de0) p.de0[gl] = lam_out;
@@ -247,19 +250,19 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     read_exclusive<G>(sP, sE, XP, XE);
 
     // ---- reverse recurrence over the thread's steps; gate and value gradients ----
-    float lam[VEC];
+    F lam[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) lam[e] = XE[e] + Q::apply(XP[e], sCarry[j * VEC + e]);
+    for (int e = 0; e < VEC; ++e) lam[e] = XE[e] + Q::apply(XP[e], F(sCarry[j * VEC + e]));
 #pragma unroll
     for (int i = L - 1; i >= 0; --i) {
         const bool ok = FULL || (lane_ok && t0 + i < p.T);
         float dav[VEC], dvv[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const float dE = Gr[i][e] + lam[e];
-            lam[e] = Q::apply(S_[i][e], dE);
-            dav[e] = dE * V_[i][e];
-            dvv[e] = MODE == kDirect ? dE : dE * S_[i][e];
+            const F dE = F(Gr[i][e]) + lam[e];
+            lam[e] = Q::apply(F(S_[i][e]), dE);
+            dav[e] = float(dE * F(V_[i][e]));
+            dvv[e] = float(MODE == kDirect ? dE : dE * F(S_[i][e]));
         }
         if constexpr (GRADS) {
             if constexpr (FULL) {
@@ -277,11 +280,12 @@ template <typename T, int MODE, int DH, int L, int NT, bool GRADS, int CHAIN>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     using G = Geom<T, DH, L, NT>;
     constexpr int CB = G::CB, TT = G::TT, NW = G::NW;
-    __shared__ __attribute__((aligned(16))) float sP[G::S * CB];  // per-slot pairs / maps
-    __shared__ __attribute__((aligned(16))) float sE[G::S * CB];
-    __shared__ float sWP[NW * CB];  // per-wave aggregates
-    __shared__ float sWE[NW * CB];
-    __shared__ float sCarry[CB];
+    using F = Acc<T>;
+    __shared__ __attribute__((aligned(16))) F sP[G::S * CB];  // per-slot pairs / maps
+    __shared__ __attribute__((aligned(16))) F sE[G::S * CB];
+    __shared__ F sWP[NW * CB];  // per-wave aggregates
+    __shared__ F sWE[NW * CB];
+    __shared__ F sCarry[CB];
 
     uint32_t rtile, cb;
     tile_of(blockIdx.x, p.nCB, rtile, cb);

@@ -465,11 +465,25 @@ __device__ __forceinline__ float gate_u_slope(float a, float& slope) {
 //   direct      x - u x + v   = s x + v
 // Both keep x's relative precision when u is small (long memory).  A masked step passes
 // u = 0 and v = 0, which leaves x unchanged.
-template <int MODE>
-__device__ __forceinline__ float update(float x, float u, float v) {
-    if constexpr (MODE == kControlled) return __builtin_fmaf(u, v - x, x);
-    else return __builtin_fmaf(-u, x, x) + v;
+// a * b + c rounded once, in the operands' own type.
+__device__ __forceinline__ float fma_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double fma_(double a, double b, double c) { return __builtin_fma(a, b, c); }
+
+template <int MODE, typename F>
+__device__ __forceinline__ F update(F x, F u, F v) {
+    if constexpr (MODE == kControlled) return fma_(u, v - x, x);
+    else return fma_(-u, x, x) + v;
 }
+
+// The type the scans accumulate in: fp64 for fp32 storage, fp32 otherwise.  fp32 storage has
+// the tightest bar (1e-5) and long-memory lanes sum thousands of roundings of the state and
+// of its reverse-time gradient, which fp32 accumulation leaves at about that size (a
+// sequential fp32 loop misses the bar there too).  On gfx950 a non-packed fp32 fma and an
+// fp64 fma issue at the same rate, so accumulating in fp64 costs registers, LDS and
+// conversions rather than issue slots; the 16- and 8-bit kernels, whose bars are 500 times
+// wider, keep fp32.  Gates, readout and look-back words stay fp32.
+template <typename T>
+using Acc = typename std::conditional<sizeof(T) == 4, double, float>::type;
 
 // Sum over the HL consecutive, aligned threads that hold one head; every thread of the head
 // receives the total.  Up to 16 threads (one DPP row) the butterfly uses DPP lane moves:
@@ -500,19 +514,19 @@ __device__ __forceinline__ float head_sum(float x) {
 // leaves an absolute error of about one unit in the last place of x in (1 - q) x, i.e.
 // relative to the state being decayed, which the parity metric's scale already covers.
 // GP<false> carries the product itself: the plain form of the same interface.
-template <bool CQ>
+template <bool CQ, typename F = float>
 struct GP;
-template <>
-struct GP<false> {
-    static constexpr float one = 1.0f;
-    __device__ static __forceinline__ float mul(float a, float b) { return a * b; }
-    __device__ static __forceinline__ float apply(float p, float x) { return p * x; }
+template <typename F>
+struct GP<false, F> {
+    static constexpr F one = F(1);
+    __device__ static __forceinline__ F mul(F a, F b) { return a * b; }
+    __device__ static __forceinline__ F apply(F p, F x) { return p * x; }
 };
-template <>
-struct GP<true> {
-    static constexpr float one = 0.0f;
-    __device__ static __forceinline__ float mul(float a, float b) { return __builtin_fmaf(-a, b, a) + b; }
-    __device__ static __forceinline__ float apply(float q, float x) { return __builtin_fmaf(-q, x, x); }
+template <typename F>
+struct GP<true, F> {
+    static constexpr F one = F(0);
+    __device__ static __forceinline__ F mul(F a, F b) { return fma_(-a, b, a) + b; }
+    __device__ static __forceinline__ F apply(F q, F x) { return fma_(-q, x, x); }
 };
 
 // Exclusive scan of the per-thread pairs over the S time slots of a tile, per channel, in
@@ -529,103 +543,117 @@ struct GP<true> {
 // maps lam_out = P lam_in + E compose the later side first; both reduce to the same update
 // (te, tp) <- (p te + e, tp p) in their own walking order, with the products in GP<CQ>'s
 // representation.
-template <class G, bool REV, bool CQ = false>
-__device__ __forceinline__ void slots_phase_a(const float* P, const float* E, float* sP, float* sE,
-                                              float* sWP, float* sWE,
-                                              float (&xp)[G::CPL][G::SPW],
-                                              float (&xe)[G::CPL][G::SPW]) {
+// N consecutive values between registers and LDS in 16-byte pieces (the address is 16-byte
+// aligned: a thread's VEC channels of one slot row).
+template <int N>
+__device__ __forceinline__ void lds_store(float* dst, const float* x) {
+#pragma unroll
+    for (int e = 0; e < N; e += 4)
+        *reinterpret_cast<float4*>(dst + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+}
+template <int N>
+__device__ __forceinline__ void lds_store(double* dst, const double* x) {
+#pragma unroll
+    for (int e = 0; e < N; e += 2) *reinterpret_cast<double2*>(dst + e) = make_double2(x[e], x[e + 1]);
+}
+template <int N>
+__device__ __forceinline__ void lds_load(const float* src, float* x) {
+#pragma unroll
+    for (int e = 0; e < N; e += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src + e);
+        x[e] = v.x;
+        x[e + 1] = v.y;
+        x[e + 2] = v.z;
+        x[e + 3] = v.w;
+    }
+}
+template <int N>
+__device__ __forceinline__ void lds_load(const double* src, double* x) {
+#pragma unroll
+    for (int e = 0; e < N; e += 2) {
+        const double2 v = *reinterpret_cast<const double2*>(src + e);
+        x[e] = v.x;
+        x[e + 1] = v.y;
+    }
+}
+
+template <class G, bool REV, bool CQ, typename F>
+__device__ __forceinline__ void slots_phase_a(const F* P, const F* E, F* sP, F* sE, F* sWP, F* sWE,
+                                              F (&xp)[G::CPL][G::SPW], F (&xe)[G::CPL][G::SPW]) {
     constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, SPW = G::SPW;
     const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
     const int j = tid % NCL, slot = tid / NCL;
-#pragma unroll
-    for (int e = 0; e < VEC; e += 4) {
-        *reinterpret_cast<float4*>(sP + slot * CB + j * VEC + e) =
-            make_float4(P[e], P[e + 1], P[e + 2], P[e + 3]);
-        *reinterpret_cast<float4*>(sE + slot * CB + j * VEC + e) =
-            make_float4(E[e], E[e + 1], E[e + 2], E[e + 3]);
-    }
+    lds_store<VEC>(sP + slot * CB + j * VEC, P);
+    lds_store<VEC>(sE + slot * CB + j * VEC, E);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int k = 0; k < G::CPL; ++k) {
         const int ch = lane + k * kWave;
-        float tp = GP<CQ>::one, te = 0.0f;
+        F tp = GP<CQ, F>::one, te = F(0);
 #pragma unroll
         for (int q = 0; q < SPW; ++q) {
             const int sw = REV ? SPW - 1 - q : q;
             const int s = w * SPW + sw;
-            const float ps = sP[s * CB + ch], es = sE[s * CB + ch];
+            const F ps = sP[s * CB + ch], es = sE[s * CB + ch];
             xp[k][sw] = tp;
             xe[k][sw] = te;
-            te = GP<CQ>::apply(ps, te) + es;
-            tp = GP<CQ>::mul(tp, ps);
+            te = GP<CQ, F>::apply(ps, te) + es;
+            tp = GP<CQ, F>::mul(tp, ps);
         }
         sWP[w * CB + ch] = tp;
         sWE[w * CB + ch] = te;
     }
 }
 
-template <class G, bool REV, bool CQ = false>
-__device__ __forceinline__ void slots_phase_b(float* sP, float* sE, const float* sWP,
-                                              const float* sWE, const float (&xp)[G::CPL][G::SPW],
-                                              const float (&xe)[G::CPL][G::SPW]) {
+template <class G, bool REV, bool CQ, typename F>
+__device__ __forceinline__ void slots_phase_b(F* sP, F* sE, const F* sWP, const F* sWE,
+                                              const F (&xp)[G::CPL][G::SPW],
+                                              const F (&xe)[G::CPL][G::SPW]) {
     constexpr int CB = G::CB, SPW = G::SPW, NW = G::NW;
     const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
 #pragma unroll
     for (int k = 0; k < G::CPL; ++k) {
         const int ch = lane + k * kWave;
-        float wp = GP<CQ>::one, we = 0.0f;  // the other waves on this slot's earlier side
+        F wp = GP<CQ, F>::one, we = F(0);  // the other waves on this slot's earlier side
 #pragma unroll
         for (int q = 0; q < NW; ++q) {
             const int v = REV ? NW - 1 - q : q;
             if (REV ? v > w : v < w) {
-                const float pv = sWP[v * CB + ch], ev = sWE[v * CB + ch];
-                we = GP<CQ>::apply(pv, we) + ev;
-                wp = GP<CQ>::mul(wp, pv);
+                const F pv = sWP[v * CB + ch], ev = sWE[v * CB + ch];
+                we = GP<CQ, F>::apply(pv, we) + ev;
+                wp = GP<CQ, F>::mul(wp, pv);
             }
         }
 #pragma unroll
         for (int sw = 0; sw < SPW; ++sw) {
             const int s = w * SPW + sw;
-            sP[s * CB + ch] = GP<CQ>::mul(xp[k][sw], wp);
-            sE[s * CB + ch] = xe[k][sw] + GP<CQ>::apply(xp[k][sw], we);
+            sP[s * CB + ch] = GP<CQ, F>::mul(xp[k][sw], wp);
+            sE[s * CB + ch] = xe[k][sw] + GP<CQ, F>::apply(xp[k][sw], we);
         }
     }
 }
 
 // Composition of all waves' aggregates for channel ch: the tile's own pair / map.
-template <class G, bool REV, bool CQ = false>
-__device__ __forceinline__ void tile_total(const float* sWP, const float* sWE, int ch, float& tp,
-                                           float& te) {
-    tp = GP<CQ>::one;
-    te = 0.0f;
+template <class G, bool REV, bool CQ, typename F>
+__device__ __forceinline__ void tile_total(const F* sWP, const F* sWE, int ch, F& tp, F& te) {
+    tp = GP<CQ, F>::one;
+    te = F(0);
 #pragma unroll
     for (int q = 0; q < G::NW; ++q) {
         const int v = REV ? G::NW - 1 - q : q;
-        const float pv = sWP[v * G::CB + ch], ev = sWE[v * G::CB + ch];
-        te = GP<CQ>::apply(pv, te) + ev;
-        tp = GP<CQ>::mul(tp, pv);
+        const F pv = sWP[v * G::CB + ch], ev = sWE[v * G::CB + ch];
+        te = GP<CQ, F>::apply(pv, te) + ev;
+        tp = GP<CQ, F>::mul(tp, pv);
     }
 }
 
 // The tile-wide exclusive pair of this thread's slot, for its VEC channels.
-template <class G>
-__device__ __forceinline__ void read_exclusive(const float* sP, const float* sE, float* XP,
-                                               float* XE) {
+template <class G, typename F>
+__device__ __forceinline__ void read_exclusive(const F* sP, const F* sE, F* XP, F* XE) {
     const int j = threadIdx.x % G::NCL, slot = threadIdx.x / G::NCL;
-#pragma unroll
-    for (int e = 0; e < G::VEC; e += 4) {
-        const float4 p = *reinterpret_cast<const float4*>(sP + slot * G::CB + j * G::VEC + e);
-        const float4 q = *reinterpret_cast<const float4*>(sE + slot * G::CB + j * G::VEC + e);
-        XP[e] = p.x;
-        XP[e + 1] = p.y;
-        XP[e + 2] = p.z;
-        XP[e + 3] = p.w;
-        XE[e] = q.x;
-        XE[e + 1] = q.y;
-        XE[e + 2] = q.z;
-        XE[e + 3] = q.w;
-    }
+    lds_load<G::VEC>(sP + slot * G::CB + j * G::VEC, XP);
+    lds_load<G::VEC>(sE + slot * G::CB + j * G::VEC, XE);
 }
 
 __device__ __forceinline__ uint64_t tag_word(uint32_t tag, float v) {
@@ -689,12 +717,16 @@ struct WalkCount {
     uint32_t polls;
 };
 
-template <bool PROD = false, uint32_t LIMIT = kSpinLimit, bool CQ = false>
-__device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t* flagY,
-                                           int64_t nLanes, int64_t lane, int64_t tile, int step,
-                                           uint32_t tagAgg, uint32_t tagInc, uint32_t* hdr,
-                                           float* pinc = nullptr, WalkCount* wc = nullptr) {
-    float ap = GP<CQ>::one, ae = 0.0f;
+//
+// F is the type the walk folds the published fp32 values in: the kernel's accumulation type
+// (Acc), so that a long walk adds no roundings of its own in the fp64-accumulating kernels.
+template <bool PROD = false, uint32_t LIMIT = kSpinLimit, bool CQ = false, typename F = float>
+__device__ __forceinline__ F look_back(const uint64_t* flagX, const uint64_t* flagY,
+                                       int64_t nLanes, int64_t lane, int64_t tile, int step,
+                                       uint32_t tagAgg, uint32_t tagInc, uint32_t* hdr,
+                                       float* pinc = nullptr, WalkCount* wc = nullptr) {
+    using Q = GP<CQ, F>;
+    F ap = Q::one, ae = F(0);
     int64_t j = tile + step;
     uint32_t polls = 0;
     for (;;) {
@@ -705,25 +737,25 @@ __device__ __forceinline__ float look_back(const uint64_t* flagX, const uint64_t
         if (tg == tagInc) {
             if constexpr (!PROD) {
                 if (wc) *wc = WalkCount{(uint32_t)((j - tile) * step - 1), polls};
-                return ae + GP<CQ>::apply(ap, word_val(x));
+                return ae + Q::apply(ap, F(word_val(x)));
             }
             // the inclusive product is published beside the inclusive state, in no fixed
             // order: wait until it is visible too
             if (word_tag(yv) == tagInc) {
-                *pinc = GP<CQ>::mul(ap, word_val(yv));
-                return ae + GP<CQ>::apply(ap, word_val(x));
+                *pinc = float(Q::mul(ap, F(word_val(yv))));
+                return ae + Q::apply(ap, F(word_val(x)));
             }
         }
         if (tg == tagAgg && word_tag(yv) == tagAgg) {
-            ae = ae + GP<CQ>::apply(ap, word_val(x));
-            ap = GP<CQ>::mul(ap, word_val(yv));
+            ae = ae + Q::apply(ap, F(word_val(x)));
+            ap = Q::mul(ap, F(word_val(yv)));
             j += step;
             continue;
         }
         if (!wait_turn<LIMIT>(++polls, hdr, tagInc)) {
             if constexpr (PROD) *pinc = __builtin_nanf("");
             if (wc) *wc = WalkCount{(uint32_t)((j - tile) * step - 1), polls};
-            return __builtin_nanf("");
+            return F(__builtin_nanf(""));
         }
     }
 }
@@ -753,20 +785,20 @@ enum : int { kChainDefault = 0, kChainDet = 1, kChainTest = 2, kChainStats = 3 }
 // With K = 1 every tile waits for its neighbour's inclusive value.  The host picks K from the
 // number of chains, so that a block's walk stays short while the inclusive values still move
 // K tiles per hop.
-template <bool PROD = false, uint32_t LIMIT = kSpinLimit, bool CQ = false>
-__device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, int64_t nLanes,
-                                             int64_t lane, int64_t tile, int step, uint32_t tagAgg,
-                                             uint32_t tagInc, uint32_t* hdr, float tp, float te,
-                                             float* pin, uint32_t det, bool pubInc,
-                                             WalkCount* wc = nullptr) {
+template <bool PROD = false, uint32_t LIMIT = kSpinLimit, bool CQ = false, typename F = float>
+__device__ __forceinline__ F chain_carry(uint64_t* flagX, uint64_t* flagY, int64_t nLanes,
+                                         int64_t lane, int64_t tile, int step, uint32_t tagAgg,
+                                         uint32_t tagInc, uint32_t* hdr, float tp, float te,
+                                         float* pin, uint32_t det, bool pubInc,
+                                         WalkCount* wc = nullptr) {
     if (det == 0u) {
         const uint64_t x = peek(flagX + (tile + step) * nLanes + lane);
         if (word_tag(x) == tagInc) {
-            if constexpr (!PROD) return word_val(x);
+            if constexpr (!PROD) return F(word_val(x));
             const uint64_t y = peek(flagY + (tile + step) * nLanes + lane);
             if (word_tag(y) == tagInc) {
                 *pin = word_val(y);
-                return word_val(x);
+                return F(word_val(x));
             }
         }
     }
@@ -775,8 +807,8 @@ __device__ __forceinline__ float chain_carry(uint64_t* flagX, uint64_t* flagY, i
         publish(flagY + tile * nLanes + lane, tagAgg, tp);
     }
     if (wc) *wc = WalkCount{0u, 0u};
-    return look_back<PROD, LIMIT, CQ>(flagX, flagY, nLanes, lane, tile, step, tagAgg, tagInc, hdr,
-                                      pin, wc);
+    return look_back<PROD, LIMIT, CQ, F>(flagX, flagY, nLanes, lane, tile, step, tagAgg, tagInc,
+                                         hdr, pin, wc);
 }
 
 // Statistics instance: adds this wave's look-back outcome to the workgroup's set of counters

@@ -19,16 +19,17 @@ namespace esa {
 template <typename T, int MODE, int DH, int L, int NT, bool READOUT, bool PROD, bool FULL,
           int CHAIN>
 __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint32_t cb,
-                                         float* sP, float* sE, float* sWP, float* sWE,
-                                         float* sCarry) {
+                                         Acc<T>* sP, Acc<T>* sE, Acc<T>* sWP, Acc<T>* sWE,
+                                         Acc<T>* sCarry) {
     using G = Geom<T, DH, L, NT>;
     constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, HL = G::HL;
     constexpr int TT = G::TT;
     constexpr int ES = sizeof(T);
     // gate products are carried as complements (GP); the segment pass converts its gate
-    // product output back to a product at the end
+    // product output back to a product at the end.  F: the accumulation type (Acc).
     constexpr bool CQ = true;
-    using Q = GP<CQ>;
+    using F = Acc<T>;
+    using Q = GP<CQ, F>;
     static_assert(kCkptChunk % L == 0, "checkpoint steps must end a thread's slot");
     const uint32_t epoch = launch_epoch(p.epoch, p.epochWord);
     const uint32_t tagAgg = make_tag(epoch, kTagAgg);
@@ -81,11 +82,11 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
     // ---- level 1: gates and the thread's own fold (identity step where masked) ----
     // U: the gate's complement 1 - s; V: the value (both 0 on a masked step)
     float U[L][VEC], V[L][VEC];
-    float P[VEC], E[VEC];
+    F P[VEC], E[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
         P[e] = Q::one;
-        E[e] = 0.0f;
+        E[e] = F(0);
     }
 #pragma unroll
     for (int i = 0; i < L; ++i) {
@@ -98,32 +99,32 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
             const float u = gate_u(av[e]);
             U[i][e] = ok ? u : 0.0f;
             V[i][e] = ok ? vv[e] : 0.0f;
-            E[e] = update<MODE>(E[e], U[i][e], V[i][e]);
-            P[e] = i == 0 ? U[i][e] : Q::mul(P[e], U[i][e]);
+            E[e] = update<MODE, F>(E[e], F(U[i][e]), F(V[i][e]));
+            P[e] = i == 0 ? F(U[i][e]) : Q::mul(P[e], F(U[i][e]));
         }
     }
 
     // ---- level 2: slot pairs through LDS (within each wave, then across the waves) ----
     const int w = tid / kWave;
-    float xp[G::CPL][G::SPW], xe[G::CPL][G::SPW];
-    slots_phase_a<G, false, CQ>(P, E, sP, sE, sWP, sWE, xp, xe);
+    F xp[G::CPL][G::SPW], xe[G::CPL][G::SPW];
+    slots_phase_a<G, false, CQ, F>(P, E, sP, sE, sWP, sWE, xp, xe);
     __syncthreads();
-    slots_phase_b<G, false, CQ>(sP, sE, sWP, sWE, xp, xe);
+    slots_phase_b<G, false, CQ, F>(sP, sE, sWP, sWE, xp, xe);
 
     // ---- level 3: decoupled look-back across tiles, wave k for channels 64k.. (lane = channel) ----
     if (w < G::CPL) {
         const int ch = (tid % kWave) + w * kWave;
-        float tp, te;
-        tile_total<G, false, CQ>(sWP, sWE, ch, tp, te);
+        F tp, te;
+        tile_total<G, false, CQ, F>(sWP, sWE, ch, tp, te);
         const int64_t gl = (int64_t)cb * CB + ch;
-        float carry = 0.0f;
+        F carry = F(0);
         constexpr bool STATS = CHAIN == kChainStats;
         WalkCount wc{~0u, 0u};  // statistics instance: set when the lane walked back
         bool active = false;
         if (FULL || gl < p.nLanes) {
             uint64_t* X = p.flagX + (int64_t)tile * p.nLanes + gl;
             uint64_t* Y = p.flagY + (int64_t)tile * p.nLanes + gl;
-            float pin = Q::one;  // PROD: product of the gates of every earlier tile
+            float pin = GP<CQ>::one;  // PROD: product of the gates of every earlier tile
             constexpr bool TEST = CHAIN == kChainTest;
             const uint32_t det = CHAIN == kChainDet || TEST ? p.det : 0u;
             const bool inc = det_publishes_inc(tile, det);
@@ -131,18 +132,18 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
                 carry = p.e0 ? p.e0[gl] : 0.0f;
             } else {
                 active = true;
-                carry = chain_carry<PROD, TEST ? kTestSpinLimit : kSpinLimit, CQ>(
-                    p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg, tagInc, p.hdr, tp, te, &pin,
-                    det, inc, STATS ? &wc : nullptr);
+                carry = chain_carry<PROD, TEST ? kTestSpinLimit : kSpinLimit, CQ, F>(
+                    p.flagX, p.flagY, p.nLanes, gl, tile, -1, tagAgg, tagInc, p.hdr, float(tp),
+                    float(te), &pin, det, inc, STATS ? &wc : nullptr);
             }
             // the test instance withholds tile 0
             const bool pub = (!TEST || tile != 0) && inc;
             if constexpr (PROD) {
-                const float prod = Q::mul(tp, pin);
-                if (pub) publish(Y, tagInc, prod);
-                if (tile == p.nTiles - 1) p.prod[gl] = CQ ? 1.0f - prod : prod;
+                const F prod = Q::mul(tp, F(pin));
+                if (pub) publish(Y, tagInc, float(prod));
+                if (tile == p.nTiles - 1) p.prod[gl] = float(CQ ? F(1) - prod : prod);
             }
-            if (pub) publish(X, tagInc, te + Q::apply(tp, carry));
+            if (pub) publish(X, tagInc, float(te + Q::apply(tp, F(carry))));
         }
         if constexpr (STATS) count_walks(p.hdr, active, wc.folded != ~0u, wc);
         sCarry[ch] = carry;
@@ -155,24 +156,25 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         // steps (t % 64 == 63) and the sequence's last step always end a slot, because 64 is
         // a multiple of L and masked steps are the identity.  This skips the per-step re-run
         // and the per-step gate arrays (measured 13 % faster at 64K context).
-        float XP[VEC], XE[VEC];
+        F XP[VEC], XE[VEC];
         read_exclusive<G>(sP, sE, XP, XE);
         const int64_t tend = (t0 + L < p.T ? t0 + L : p.T) - 1;
         if ((FULL || lane_ok) && t0 < p.T) {
+            float Ef[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
-                E[e] = E[e] + Q::apply(P[e], XE[e] + Q::apply(XP[e], sCarry[j * VEC + e]));
+                Ef[e] = float(E[e] + Q::apply(P[e], XE[e] + Q::apply(XP[e], F(sCarry[j * VEC + e]))));
             if (p.ckpt && (((tend + 1) % kCkptChunk) == 0 || tend == p.T - 1)) {
                 float* dst = p.ckpt + (b * p.nck + tend / kCkptChunk) * p.C + c;
 #pragma unroll
                 for (int e = 0; e < VEC; e += 4)
-                    *reinterpret_cast<float4*>(dst + e) = make_float4(E[e], E[e + 1], E[e + 2], E[e + 3]);
+                    *reinterpret_cast<float4*>(dst + e) = make_float4(Ef[e], Ef[e + 1], Ef[e + 2], Ef[e + 3]);
             }
             if (p.eT && tend == p.T - 1) {
                 float* dst = p.eT + lane0;
 #pragma unroll
                 for (int e = 0; e < VEC; e += 4)
-                    *reinterpret_cast<float4*>(dst + e) = make_float4(E[e], E[e + 1], E[e + 2], E[e + 3]);
+                    *reinterpret_cast<float4*>(dst + e) = make_float4(Ef[e], Ef[e + 1], Ef[e + 2], Ef[e + 3]);
             }
         }
         return;
@@ -180,21 +182,22 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
 
     // ---- carry in, re-run the recurrence, readout ----
     {
-        float XP[VEC], XE[VEC];
+        F XP[VEC], XE[VEC];
         read_exclusive<G>(sP, sE, XP, XE);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) E[e] = XE[e] + Q::apply(XP[e], sCarry[j * VEC + e]);
+        for (int e = 0; e < VEC; ++e) E[e] = XE[e] + Q::apply(XP[e], F(sCarry[j * VEC + e]));
     }
     const int64_t ckbase = b * p.nck;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
         const int64_t t = t0 + i;
         const bool ok = FULL || (lane_ok && t < p.T);
-        float ss = 0.0f;
+        float ss = 0.0f, Ef[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            E[e] = update<MODE>(E[e], U[i][e], V[i][e]);
-            ss += E[e] * E[e];
+            E[e] = update<MODE, F>(E[e], F(U[i][e]), F(V[i][e]));
+            Ef[e] = float(E[e]);
+            ss += Ef[e] * Ef[e];
         }
         if constexpr (READOUT) {
             ss = head_sum<HL>(ss);
@@ -202,7 +205,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
             float qv[VEC], yv[VEC];
             unpack<T>(rq[i], qv);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) yv[e] = qv[e] * (E[e] * r);
+            for (int e = 0; e < VEC; ++e) yv[e] = qv[e] * (Ef[e] * r);
             if constexpr (FULL)
                 stbuf<T>(static_cast<char*>(p.y) + row0 + i * rstride, voff, pack<T>(yv));
             else if (ok)
@@ -212,13 +215,13 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
             float* dst = p.ckpt + (ckbase + t / kCkptChunk) * p.C + c;
 #pragma unroll
             for (int e = 0; e < VEC; e += 4)
-                *reinterpret_cast<float4*>(dst + e) = make_float4(E[e], E[e + 1], E[e + 2], E[e + 3]);
+                *reinterpret_cast<float4*>(dst + e) = make_float4(Ef[e], Ef[e + 1], Ef[e + 2], Ef[e + 3]);
         }
         if (ok && p.eT && t == p.T - 1) {
             float* dst = p.eT + lane0;
 #pragma unroll
             for (int e = 0; e < VEC; e += 4)
-                *reinterpret_cast<float4*>(dst + e) = make_float4(E[e], E[e + 1], E[e + 2], E[e + 3]);
+                *reinterpret_cast<float4*>(dst + e) = make_float4(Ef[e], Ef[e + 1], Ef[e + 2], Ef[e + 3]);
         }
     }
 }
@@ -228,11 +231,12 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     static_assert(!(READOUT && PROD), "the gate product comes from the state-only pass");
     using G = Geom<T, DH, L, NT>;
     constexpr int CB = G::CB, TT = G::TT, NW = G::NW, S = G::S;
-    __shared__ __attribute__((aligned(16))) float sP[S * CB];  // per-slot pairs
-    __shared__ __attribute__((aligned(16))) float sE[S * CB];
-    __shared__ float sWP[NW * CB];  // per-wave aggregate pairs
-    __shared__ float sWE[NW * CB];
-    __shared__ float sCarry[CB];
+    using F = Acc<T>;
+    __shared__ __attribute__((aligned(16))) F sP[S * CB];  // per-slot pairs
+    __shared__ __attribute__((aligned(16))) F sE[S * CB];
+    __shared__ F sWP[NW * CB];  // per-wave aggregate pairs
+    __shared__ F sWE[NW * CB];
+    __shared__ F sCarry[CB];
 
     uint32_t tile, cb;
     tile_of(blockIdx.x, p.nCB, tile, cb);

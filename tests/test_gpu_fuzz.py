@@ -35,13 +35,10 @@ def case_of(seed):
 
 
 def retentive_case_of(seed):
-    """Long-memory gates: mean logit 6 (about 400 steps of memory) for every storage, and 8
-    (about 3000 steps) for the 16-bit and 8-bit ones.  fp32 at mean logit 8 sits at the
-    precision of fp32 arithmetic itself (a sequential fp32 loop on the host misses the 1e-5
-    bar there too), so this set leaves it out; test_fp32_retentive_gates_do_not_drift holds
-    fp32 with still longer memory to a stated bar."""
+    """Long-memory gates, mean logit 6 or 8 (about 400 or 3000 steps of memory), for every
+    storage dtype, fp32 included."""
     c = case_of(10_000 + seed)
-    c["a_mean"] = 6.0 if c["dtype"] == torch.float32 else random.Random(seed).choice([6.0, 8.0])
+    c["a_mean"] = random.Random(seed).choice([6.0, 8.0])
     c["a_std"] = random.Random(seed + 1).choice([0.5, 1.0, 2.0])
     return c
 

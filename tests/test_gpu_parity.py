@@ -182,14 +182,12 @@ def test_fp32_gate_near_one_is_correctly_rounded(a_mean):
 @pytest.mark.parametrize("mode", ["direct", "controlled"])
 def test_fp32_retentive_gates_do_not_drift(mode):
     """fp32 storage with very retentive gates (a ~ N(10, 1): 1 - s ~ 5e-5, ~20000 steps of
-    memory) over 15000 steps, the whole sequence one chain of 59 forward tiles.  Gate
-    products of factors that close to 1 are carried as complements, so the state does not
-    drift along the sequence: y, the final state and the initial-state gradient meet the
-    fp32 bar (1e-5), and the gate, value and query gradients stay within 2e-5.  (With plain
-    products y drifted by up to 1.3e-4 and the gate gradient by up to 4.9e-4 on these
-    inputs; a sequential fp32 loop on the host, with correctly rounded gates, is off by up
-    to 3.5e-5 in y and 1.5e-4 in the gate gradient: fp32 arithmetic itself is at the bar
-    here.)"""
+    memory) over 15000 steps, the whole sequence one chain of 118 forward tiles.  Gate
+    products are carried as complements and the fp32 kernels accumulate the state and its
+    reverse-time gradient in fp64, so every output meets the fp32 bar (1e-5).  (A sequential
+    fp32 loop on the host, with correctly rounded gates, is off by up to 3.5e-5 in y and
+    1.5e-4 in the gate gradient on these inputs; with plain products and fp32 accumulation
+    the kernels drifted to 1.3e-4 in y and 4.9e-4 in the gate gradient.)"""
     say(f"fp32 retentive gates {mode}")
     B, T, H, Dh = 2, 15000, 2, 64
     m = 0 if mode == "direct" else 1
@@ -203,12 +201,9 @@ def test_fp32_retentive_gates_do_not_drift(mode):
     torch.cuda.synchronize()
     ry, reT = oracle.scan_fwd(x["a"], x["v"], x["q"], e0, mode=m)
     rda, rdv, rdq, rde0 = oracle.scan_bwd(x["a"], x["v"], x["q"], x["d"], e0, None, mode=m)
-    for name, got, ref, bar in (("y", y, ry, 1e-5), ("final_state", eT, reT, 1e-5),
-                                ("d_init", de0, rde0, 1e-5), ("d_logit", da, rda, 2e-5),
-                                ("d_value", dv, rdv, 2e-5), ("d_query", dq, rdq, 2e-5)):
-        e = err(got, ref)
-        say(f"  {name}: {e:.2e}")
-        assert e <= bar, (name, e)
+    for name, got, ref in (("y", y, ry), ("final_state", eT, reT), ("d_init", de0, rde0),
+                           ("d_logit", da, rda), ("d_value", dv, rdv), ("d_query", dq, rdq)):
+        assert_close(name, got, ref, torch.float32)
 
 
 def test_step_plan_matches_oracle_and_checks_its_tensors():
