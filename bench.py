@@ -66,11 +66,13 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="0 = min(16, cpu count)")
-    ap.add_argument("--only", choices=["train", "decode", "variants", "all", "copy", "workloads"],
+    ap.add_argument("--only", choices=["train", "decode", "variants", "all", "copy", "workloads",
+                                       "lookback"],
                     default="all",
                     help="copy: a plain 4 GiB device copy, the reference for HBM counters; "
                          "variants: the fp8 and sequence-segment variants; "
-                         "workloads: every synthetic workload's GPU time and oracle rate")
+                         "workloads: every synthetic workload's GPU time and oracle rate; "
+                         "lookback: the look-back statistics of the 64K-context scans")
     return ap.parse_args()
 
 
@@ -476,6 +478,53 @@ def bench_workloads(args, torch, binding, synth):
     return out
 
 
+def bench_lookback(args, torch, binding, synth):
+    """What the cross-tile look-back did in the 64K-context scans (fp16 and fp8 E4M3), from
+    the statistics instance of the kernels (ESA_LOOKBACK_STATS): per launch, the lanes that
+    found their neighbouring tile's inclusive value published, the lanes that walked back, the
+    tiles those walks folded, the longest walk and the unproductive polls.  Each launch is
+    also timed (HIP events) beside a launch of the default instance."""
+    out = {}
+    for name in ("long64k_f16", "long64k_f8e4m3"):
+        wl = synth.WORKLOADS[name]
+        B, T, H, Dh = wl.B, wl.T, wl.H, wl.Dh
+        log(f"[bench] look-back statistics {name}")
+        g = synth.make_inputs(wl, device="cuda:0", with_dy=True)
+        ws = torch.zeros(binding.workspace_bytes(B, T, H, Dh, g["a"].dtype), dtype=torch.uint8,
+                         device="cuda:0")
+        y = torch.empty_like(g["a"])
+        m = binding.MODES[wl.mode]
+        rec = {}
+        ck = binding.scan_fwd(g["a"], g["v"], g["q"], mode=m, return_ckpt=True, y=y,
+                              workspace=ws)[2]
+        for kind in ("fwd", "bwd"):
+            runs = []
+            for r in range(args.steps if args.steps <= 5 else 5):
+                for mode, label in ((m | binding.LOOKBACK_STATS, "stats"), (m, "default")):
+                    ws.zero_()
+                    e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                    e0.record()
+                    if kind == "fwd":
+                        binding.scan_fwd(g["a"], g["v"], g["q"], mode=mode, return_ckpt=True,
+                                         y=y, workspace=ws)
+                    else:
+                        binding.scan_bwd(g["a"], g["v"], g["q"], g["dy"], ckpt=ck, mode=mode,
+                                         workspace=ws)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    st = binding.workspace_status(ws)
+                    st["ms"] = round(e0.elapsed_time(e1), 4)
+                    if label == "stats":
+                        runs.append(st)
+                    else:
+                        runs[-1]["default_ms"] = st["ms"]
+            rec[kind] = runs
+        out[name] = rec
+        del g, y, ws, ck
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_copy(args, torch):
     """A plain device-to-device copy of 4 GiB: reads and writes exactly 4 GiB each, the
     reference that scales the HBM traffic counters (FETCH_SIZE, WRITE_SIZE)."""
@@ -517,6 +566,10 @@ def main():
         return
     if args.only == "workloads":
         result["workloads"] = bench_workloads(args, torch, binding, synth)
+        print(json.dumps(result), flush=True)
+        return
+    if args.only == "lookback":
+        result["lookback"] = bench_lookback(args, torch, binding, synth)
         print(json.dumps(result), flush=True)
         return
     if args.only in ("train", "all"):
