@@ -132,8 +132,9 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
             }
             S_[i][e] = ok ? u : 0.0f;
             V_[i][e] = ok ? V_[i][e] : 0.0f;
-            E[e] = update<MODE, F>(E[e], F(S_[i][e]), F(V_[i][e]));
-            P[e] = i == 0 ? F(S_[i][e]) : Q::mul(P[e], F(S_[i][e]));
+            const F s = F(1) - F(S_[i][e]);
+            E[e] = update<F>(E[e], s, step_b<MODE, F>(F(S_[i][e]), F(V_[i][e])));
+            P[e] = i == 0 ? F(S_[i][e]) : fma_(P[e], s, F(S_[i][e]));  // Q::mul(P, u)
         }
     }
 
@@ -148,7 +149,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     __syncthreads();
     read_exclusive<G>(sP, sE, XP, XE);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) E[e] = XE[e] + Q::apply(XP[e], F(cin[e]));
+    for (int e = 0; e < VEC; ++e) E[e] = Q::comp(XP[e], F(cin[e]), XE[e]);
 
     // ---- re-run the forward per step; readout backward; keep gE and the gate factor ----
     float Gr[L][VEC];
@@ -160,7 +161,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             Eprev[e] = E[e];
-            E[e] = update<MODE, F>(E[e], F(S_[i][e]), F(V_[i][e]));
+            E[e] = update<F>(E[e], F(1) - F(S_[i][e]), step_b<MODE, F>(F(S_[i][e]), F(V_[i][e])));
             Ef[e] = float(E[e]);
             ss += Ef[e] * Ef[e];
         }
@@ -203,7 +204,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
 #pragma unroll
         for (int i = L - 1; i >= 0; --i) {
             er = Q::apply(F(S_[i][e]), F(Gr[i][e]) + er);
-            pr = i == L - 1 ? F(S_[i][e]) : Q::mul(F(S_[i][e]), pr);
+            pr = i == L - 1 ? F(S_[i][e]) : Q::mul(pr, F(S_[i][e]));
         }
         P[e] = pr;
         E[e] = er;
@@ -238,7 +239,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
                     p.flagX, p.flagY, p.nLanes, gl, tile, +1, tagAgg, tagInc, p.hdr, float(tp),
                     float(te), &pin, det, inc, STATS ? &wc : nullptr);
             }
-            const float lam_out = float(te + Q::apply(tp, F(carry)));
+            const float lam_out = float(Q::comp(tp, F(carry), te));
             // the test instance withholds the last tile
             if ((!TEST || tile != p.nTiles - 1) && inc) publish(X, tagInc, lam_out);
             if (tile == 0 && p.de0) p.de0[gl] = lam_out;
@@ -252,7 +253,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     // ---- reverse recurrence over the thread's steps; gate and value gradients ----
     F lam[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) lam[e] = XE[e] + Q::apply(XP[e], F(sCarry[j * VEC + e]));
+    for (int e = 0; e < VEC; ++e) lam[e] = Q::comp(XP[e], F(sCarry[j * VEC + e]), XE[e]);
 #pragma unroll
     for (int i = L - 1; i >= 0; --i) {
         const bool ok = FULL || (lane_ok && t0 + i < p.T);

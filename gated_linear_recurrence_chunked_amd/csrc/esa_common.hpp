@@ -460,20 +460,22 @@ __device__ __forceinline__ float gate_u_slope(float a, float& slope) {
     return u;
 }
 
-// One step of the recurrence on the state x with the gate's complement u (see GP):
-//   controlled  x + u (v - x) = s x + (1 - s) v
-//   direct      x - u x + v   = s x + v
-// Both keep x's relative precision when u is small (long memory).  A masked step passes
-// u = 0 and v = 0, which leaves x unchanged.
 // a * b + c rounded once, in the operands' own type.
 __device__ __forceinline__ float fma_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
 __device__ __forceinline__ double fma_(double a, double b, double c) { return __builtin_fma(a, b, c); }
 
+// One step of the recurrence on the state x: x' = s x + b with s = 1 - u, b = u v (controlled)
+// or v (direct), one fma on x.  s = 1 - u is exact for u >= 1/2 and otherwise rounds by at
+// most 2^-25 (unbiased), i.e. one rounding relative to x as in any update; u itself (the
+// complement, relatively exact) is what the gate products use (see GP).  A masked step passes
+// s = 1, b = 0, which leaves x unchanged.
 template <int MODE, typename F>
-__device__ __forceinline__ F update(F x, F u, F v) {
-    if constexpr (MODE == kControlled) return fma_(u, v - x, x);
-    else return fma_(-u, x, x) + v;
+__device__ __forceinline__ F step_b(F u, F v) {
+    if constexpr (MODE == kControlled) return u * v;
+    else return v;
 }
+template <typename F>
+__device__ __forceinline__ F update(F x, F s, F b) { return fma_(s, x, b); }
 
 // The type the scans accumulate in: fp64 for fp32 storage, fp32 otherwise.  fp32 storage has
 // the tightest bar (1e-5) and long-memory lanes sum thousands of roundings of the state and
@@ -516,17 +518,30 @@ __device__ __forceinline__ float head_sum(float x) {
 // GP<false> carries the product itself: the plain form of the same interface.
 template <bool CQ, typename F = float>
 struct GP;
+//
+// Operations (p, q: products in the representation; x, e: states):
+//   mul(a, b)      the product of two gate products
+//   apply(p, x)    p x
+//   comp(p, x, e)  e + p x, the pair combine's state part
+// For complements, mul is q1 + q2 - q1 q2 = q1 (1 - q2) + q2 and comp is (1 - q) x + e, each
+// one fma on the running value a or x, after a subtraction that does not depend on it (so a
+// serial fold is one dependent fma per step).  1 - q is exact for q >= 1/2 and rounds by at
+// most 2^-25 below; that error is multiplied by a <= 1 (relative to the result, at most
+// 2^-25) or by x (relative to x, as any rounding of the state), and it is unbiased, unlike the
+// product of two near-one factors.
 template <typename F>
 struct GP<false, F> {
     static constexpr F one = F(1);
     __device__ static __forceinline__ F mul(F a, F b) { return a * b; }
     __device__ static __forceinline__ F apply(F p, F x) { return p * x; }
+    __device__ static __forceinline__ F comp(F p, F x, F e) { return fma_(p, x, e); }
 };
 template <typename F>
 struct GP<true, F> {
     static constexpr F one = F(0);
-    __device__ static __forceinline__ F mul(F a, F b) { return fma_(-a, b, a) + b; }
+    __device__ static __forceinline__ F mul(F a, F b) { return fma_(a, F(1) - b, b); }
     __device__ static __forceinline__ F apply(F q, F x) { return fma_(-q, x, x); }
+    __device__ static __forceinline__ F comp(F q, F x, F e) { return fma_(F(1) - q, x, e); }
 };
 
 // Exclusive scan of the per-thread pairs over the S time slots of a tile, per channel, in
@@ -598,7 +613,7 @@ __device__ __forceinline__ void slots_phase_a(const F* P, const F* E, F* sP, F* 
             const F ps = sP[s * CB + ch], es = sE[s * CB + ch];
             xp[k][sw] = tp;
             xe[k][sw] = te;
-            te = GP<CQ, F>::apply(ps, te) + es;
+            te = GP<CQ, F>::comp(ps, te, es);
             tp = GP<CQ, F>::mul(tp, ps);
         }
         sWP[w * CB + ch] = tp;
@@ -621,7 +636,7 @@ __device__ __forceinline__ void slots_phase_b(F* sP, F* sE, const F* sWP, const 
             const int v = REV ? NW - 1 - q : q;
             if (REV ? v > w : v < w) {
                 const F pv = sWP[v * CB + ch], ev = sWE[v * CB + ch];
-                we = GP<CQ, F>::apply(pv, we) + ev;
+                we = GP<CQ, F>::comp(pv, we, ev);
                 wp = GP<CQ, F>::mul(wp, pv);
             }
         }
@@ -629,7 +644,7 @@ __device__ __forceinline__ void slots_phase_b(F* sP, F* sE, const F* sWP, const 
         for (int sw = 0; sw < SPW; ++sw) {
             const int s = w * SPW + sw;
             sP[s * CB + ch] = GP<CQ, F>::mul(xp[k][sw], wp);
-            sE[s * CB + ch] = xe[k][sw] + GP<CQ, F>::apply(xp[k][sw], we);
+            sE[s * CB + ch] = GP<CQ, F>::comp(xp[k][sw], we, xe[k][sw]);
         }
     }
 }
@@ -643,7 +658,7 @@ __device__ __forceinline__ void tile_total(const F* sWP, const F* sWE, int ch, F
     for (int q = 0; q < G::NW; ++q) {
         const int v = REV ? G::NW - 1 - q : q;
         const F pv = sWP[v * G::CB + ch], ev = sWE[v * G::CB + ch];
-        te = GP<CQ, F>::apply(pv, te) + ev;
+        te = GP<CQ, F>::comp(pv, te, ev);
         tp = GP<CQ, F>::mul(tp, pv);
     }
 }
@@ -737,17 +752,17 @@ __device__ __forceinline__ F look_back(const uint64_t* flagX, const uint64_t* fl
         if (tg == tagInc) {
             if constexpr (!PROD) {
                 if (wc) *wc = WalkCount{(uint32_t)((j - tile) * step - 1), polls};
-                return ae + Q::apply(ap, F(word_val(x)));
+                return Q::comp(ap, F(word_val(x)), ae);
             }
             // the inclusive product is published beside the inclusive state, in no fixed
             // order: wait until it is visible too
             if (word_tag(yv) == tagInc) {
                 *pinc = float(Q::mul(ap, F(word_val(yv))));
-                return ae + Q::apply(ap, F(word_val(x)));
+                return Q::comp(ap, F(word_val(x)), ae);
             }
         }
         if (tg == tagAgg && word_tag(yv) == tagAgg) {
-            ae = ae + Q::apply(ap, F(word_val(x)));
+            ae = Q::comp(ap, F(word_val(x)), ae);
             ap = Q::mul(ap, F(word_val(yv)));
             j += step;
             continue;

@@ -80,8 +80,12 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
     }
 
     // ---- level 1: gates and the thread's own fold (identity step where masked) ----
-    // U: the gate's complement 1 - s; V: the value (both 0 on a masked step)
-    float U[L][VEC], V[L][VEC];
+    // Each step is x' = s x + b (update()).  With fp32 accumulation SB[i] holds s = 1 - u and
+    // WB[i] the write term b, so the re-run below is one fma per step; with fp64 accumulation
+    // they hold u and v, and s and b are formed in fp64 at each use (an fp32 s would round).
+    // A masked step holds s = 1, b = 0 (u = 0, v = 0).
+    constexpr bool WIDE = std::is_same<F, double>::value;
+    float SB[L][VEC], WB[L][VEC];
     F P[VEC], E[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -96,11 +100,13 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         unpack<T>(rv[i], vv);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const float u = gate_u(av[e]);
-            U[i][e] = ok ? u : 0.0f;
-            V[i][e] = ok ? vv[e] : 0.0f;
-            E[e] = update<MODE, F>(E[e], F(U[i][e]), F(V[i][e]));
-            P[e] = i == 0 ? F(U[i][e]) : Q::mul(P[e], F(U[i][e]));
+            const float u = ok ? gate_u(av[e]) : 0.0f;
+            const float v = ok ? vv[e] : 0.0f;
+            const F s = F(1) - F(u), b = step_b<MODE, F>(F(u), F(v));
+            SB[i][e] = WIDE ? u : float(s);
+            WB[i][e] = WIDE ? v : float(b);
+            E[e] = update<F>(E[e], s, b);
+            P[e] = i == 0 ? F(u) : fma_(P[e], s, F(u));  // Q::mul(P, u) with s = 1 - u
         }
     }
 
@@ -143,7 +149,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
                 if (pub) publish(Y, tagInc, float(prod));
                 if (tile == p.nTiles - 1) p.prod[gl] = float(CQ ? F(1) - prod : prod);
             }
-            if (pub) publish(X, tagInc, float(te + Q::apply(tp, F(carry))));
+            if (pub) publish(X, tagInc, float(Q::comp(tp, F(carry), te)));
         }
         if constexpr (STATS) count_walks(p.hdr, active, wc.folded != ~0u, wc);
         sCarry[ch] = carry;
@@ -163,7 +169,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
             float Ef[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
-                Ef[e] = float(E[e] + Q::apply(P[e], XE[e] + Q::apply(XP[e], F(sCarry[j * VEC + e]))));
+                Ef[e] = float(Q::comp(P[e], Q::comp(XP[e], F(sCarry[j * VEC + e]), XE[e]), E[e]));
             if (p.ckpt && (((tend + 1) % kCkptChunk) == 0 || tend == p.T - 1)) {
                 float* dst = p.ckpt + (b * p.nck + tend / kCkptChunk) * p.C + c;
 #pragma unroll
@@ -185,7 +191,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         F XP[VEC], XE[VEC];
         read_exclusive<G>(sP, sE, XP, XE);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) E[e] = XE[e] + Q::apply(XP[e], F(sCarry[j * VEC + e]));
+        for (int e = 0; e < VEC; ++e) E[e] = Q::comp(XP[e], F(sCarry[j * VEC + e]), XE[e]);
     }
     const int64_t ckbase = b * p.nck;
 #pragma unroll
@@ -195,7 +201,10 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         float ss = 0.0f, Ef[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            E[e] = update<MODE, F>(E[e], F(U[i][e]), F(V[i][e]));
+            if constexpr (WIDE)
+                E[e] = update<F>(E[e], F(1) - F(SB[i][e]), step_b<MODE, F>(F(SB[i][e]), F(WB[i][e])));
+            else
+                E[e] = update<F>(E[e], F(SB[i][e]), F(WB[i][e]));
             Ef[e] = float(E[e]);
             ss += Ef[e] * Ef[e];
         }

@@ -43,7 +43,8 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     float ss = 0.0f;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-        st[e] = update<MODE, float>(st[e], gate_u(av[e]), vv[e]);
+        const float u = gate_u(av[e]);
+        st[e] = update<float>(st[e], 1.0f - u, step_b<MODE, float>(u, vv[e]));
         ss += st[e] * st[e];
     }
     ss = head_sum<HL>(ss);
