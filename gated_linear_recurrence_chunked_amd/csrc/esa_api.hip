@@ -27,11 +27,13 @@ struct Problem {
 
 struct TileShape {
     int CB, TTf, TTb;
+    int TTf1;  // tile length of forward variant 1, or 0 where it is not built
 };
 
 template <typename T, int DH>
 TileShape tile_shape_of() {
-    return TileShape{FwdCfg<T, DH>::G::CB, FwdCfg<T, DH>::G::TT, BwdCfg<T, DH>::G::TT};
+    return TileShape{FwdCfg<T, DH>::G::CB, FwdCfg<T, DH>::G::TT, BwdCfg<T, DH>::G::TT,
+                     kHasFwdVariant<T, DH> ? FwdCfg<T, DH, 1>::G::TT : 0};
 }
 
 template <typename T>
@@ -113,17 +115,49 @@ int check_test_flag(const Problem& pr, bool call_allows_it) {
 
 struct Layout {
     uint32_t nCB, nTilesF, nTilesB;
+    uint32_t fwdVariant, nTilesFV;  // the readout forward's tile-shape variant and its tiles
     int64_t nck;
     size_t offX, offY, offCk, total;
 };
+
+// The readout forward's tile-shape table (fp16 storage, Dh = 64, the default look-back): the
+// problem classes -- the powers of two at or above the channel-block count and the sequence
+// length -- where the 256-thread forward (128-step tiles, FwdCfg variant 1) ran faster than
+// the 512-thread one (256-step tiles), by 4-10 %, in A/B sweeps of both on two boxes over
+// 1-256 batch rows of 512 channels and 512-65536 steps.  Everything else, the 64K-context
+// workload included, takes the 512-thread forward.  Chosen from the sizes alone, so a problem
+// always runs the same kernels.
+struct FwdTileClass {
+    uint8_t lgCB, lgT;
+};
+constexpr FwdTileClass kFwd256[] = {{3, 9},  {3, 10},  {3, 11},  {5, 9},  {5, 10},
+                                    {8, 14}, {9, 10},  {9, 11},  {9, 13}, {9, 14},
+                                    {10, 12}, {10, 13}, {11, 9}, {11, 11}};
+
+int ceil_log2(int64_t x) {
+    int k = 0;
+    while (k < 62 && (int64_t(1) << k) < x) ++k;
+    return k;
+}
+
+uint32_t fwd_tile_variant(const Problem& pr, int64_t nCB) {
+    if (pr.dtype != ESA_F16 || pr.Dh != 64 || pr.forceTimeout || pr.stats) return 0;
+    const int lc = ceil_log2(nCB), lt = ceil_log2(pr.T);
+    for (const FwdTileClass& c : kFwd256)
+        if (c.lgCB == lc && c.lgT == lt) return 1;
+    return 0;
+}
 
 // Workspace: [header 256 B][X words: nTiles x nLanes x 8 B][Y words: same][checkpoint].
 int layout_of(const Problem& pr, Layout* L) {
     const TileShape ts = tile_shape(pr.dtype, pr.Dh);
     const int64_t nCB = cdiv(pr.nLanes, ts.CB);
+    const uint32_t var = ts.TTf1 ? fwd_tile_variant(pr, nCB) : 0;
     const int64_t nTF = pr.T > 0 ? cdiv(pr.T, ts.TTf) : 0;
+    const int64_t nTFV = var ? (pr.T > 0 ? cdiv(pr.T, ts.TTf1) : 0) : nTF;
     const int64_t nTB = pr.T > 0 ? cdiv(pr.T, ts.TTb) : 0;
-    const int64_t nTM = nTF > nTB ? nTF : nTB;
+    int64_t nTM = nTF > nTB ? nTF : nTB;
+    nTM = nTFV > nTM ? nTFV : nTM;
     int64_t nwg, words, xbytes, ckbytes;
     if (!mul64(nCB, nTM, &nwg) || nwg > (int64_t)INT32_MAX)
         return ESA_ERR_UNSUPPORTED;
@@ -131,6 +165,8 @@ int layout_of(const Problem& pr, Layout* L) {
     L->nCB = (uint32_t)nCB;
     L->nTilesF = (uint32_t)nTF;
     L->nTilesB = (uint32_t)nTB;
+    L->fwdVariant = var;
+    L->nTilesFV = (uint32_t)nTFV;
     L->nck = cdiv(pr.T, kCkptChunk);
     if (!mul64(L->nck, pr.nLanes, &ckbytes) || !mul64(ckbytes, 4, &ckbytes)) return ESA_ERR_UNSUPPORTED;
     L->offX = 256;
@@ -424,7 +460,7 @@ int scan_fwd_impl(bool noalloc, int64_t B, int64_t T, int64_t H, int64_t Dh, int
     const Range out[] = {{y, seq}, {final_state, st}, {ckpt, ckb}, {workspace, workspace_bytes}};
     if (any_overlap(in, 4, out, 4)) return ESA_ERR_INVALID_ARG;
     // look-back words of the forward alone: header, X and Y over the forward's tiles
-    const size_t xbytes = align256((size_t)L.nTilesF * (size_t)pr.nLanes * 8);
+    const size_t xbytes = align256((size_t)L.nTilesFV * (size_t)pr.nLanes * 8);
     size_t offY = L.offY;
     if (noalloc) {
         if (T > 0 && 256 + 2 * xbytes > (size_t)ESA_NOALLOC_SCRATCH_BYTES) return ESA_ERR_SCRATCH_LIMIT;
@@ -461,10 +497,11 @@ int scan_fwd_impl(bool noalloc, int64_t B, int64_t T, int64_t H, int64_t Dh, int
     p.nLanes = pr.nLanes;
     p.nck = L.nck;
     p.nCB = L.nCB;
-    p.nTiles = L.nTilesF;
+    p.nTiles = L.nTilesFV;
     p.det = det_block(pr, L.nCB);
     p.withhold = pr.forceTimeout;
     p.stats = pr.stats;
+    p.variant = L.fwdVariant;
     rc = set_epoch(s, p.hdr, &p.epoch, &p.epochWord);
     if (rc != ESA_OK) return rc;
     return hip_status(ESA_DISPATCH(fwd, dtype, pr.mode, Dh, p, s));

@@ -125,12 +125,18 @@ struct Geom {
 // step: 16 channels over two steps (256-thread forward workgroups, three to a CU) measured 6 %
 // (forward) and 13 % (backward) slower at 64K context, with twice the slot-scan and
 // look-back work per element and 16-channel thread spans whose LDS accesses collide in banks.
-template <typename T, int DH>
+//
+// Variant V = 1 of the forward takes 256-thread workgroups (tiles of half the depth).  The
+// host picks it from a measured table (fwd_tile_variant in the dispatcher) for the problem
+// sizes where it ran faster; it is built for fp16 storage with Dh = 64, where it was measured.
+template <typename T, int DH, int V = 0>
 struct FwdCfg {
-    static constexpr int NT = 512;
+    static constexpr int NT = V == 0 ? 512 : 256;
     static constexpr int L = 4;
     using G = Geom<T, DH, L, NT>;
 };
+template <typename T, int DH>
+constexpr bool kHasFwdVariant = std::is_same<T, _Float16>::value && DH == 64;
 template <typename T, int DH>
 struct BwdCfg {
     static constexpr int NT = 256;
@@ -193,6 +199,7 @@ struct FwdParams {
     uint32_t det;    // 0, or the block of the reproducible look-back (a power of two)
     uint32_t withhold;  // non-zero: launch the forced-timeout test instance (see launch_fwd)
     uint32_t stats;     // non-zero: launch the look-back statistics instance
+    uint32_t variant;   // tile-shape variant of FwdCfg (0 default, 1 where kHasFwdVariant)
 };
 
 struct BwdParams {

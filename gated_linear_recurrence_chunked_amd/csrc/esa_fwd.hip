@@ -261,9 +261,9 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
                                                                   sCarry);
 }
 
-template <typename T, int MODE, int DH, int CHAIN>
+template <typename T, int MODE, int DH, int CHAIN, int V = 0>
 hipError_t launch_fwd_as(const FwdParams& p, hipStream_t s) {
-    using C = FwdCfg<T, DH>;
+    using C = FwdCfg<T, DH, V>;
     const dim3 grid(p.nCB * p.nTiles), block(C::NT);
     if (p.y)
         hipLaunchKernelGGL((fwd_kernel<T, MODE, DH, C::L, C::NT, true, false, CHAIN>), grid, block,
@@ -304,6 +304,12 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
             return hipErrorNotSupported;
         }
     }
+    if constexpr (kHasFwdVariant<T, DH>) {
+        if (p.variant == 1)
+            return p.det ? launch_fwd_as<T, MODE, DH, kChainDet, 1>(p, s)
+                         : launch_fwd_as<T, MODE, DH, kChainDefault, 1>(p, s);
+    }
+    if (p.variant != 0) return hipErrorNotSupported;
     return p.det ? launch_fwd_as<T, MODE, DH, kChainDet>(p, s)
                  : launch_fwd_as<T, MODE, DH, kChainDefault>(p, s);
 }

@@ -195,8 +195,9 @@ int esa_scan_fwd(int64_t B, int64_t T, int64_t H, int64_t Dh, int dtype, int mod
  * workspace.  Its look-back words live in a static device array of ESA_NOALLOC_SCRATCH_BYTES
  * that every device the library runs on holds until the process ends; the call allocates
  * nothing.  The problem needs 256 + 2 * ceil(T / TT) * B * H * Dh * 8 bytes of it, TT being
- * the forward's tile length in steps: 256 (16-bit storage, Dh <= 64), 128 (16-bit with
- * Dh = 128, 8-bit, fp32 with Dh <= 64) or 64 (fp32 with Dh = 128);
+ * the forward's tile length in steps: 256 (16-bit storage, Dh <= 64; 128 for the fp16,
+ * Dh = 64 sizes that the forward's measured tile table gives 256-thread workgroups), 128
+ * (16-bit with Dh = 128, 8-bit, fp32 with Dh <= 64) or 64 (fp32 with Dh = 128);
  * esa_scan_workspace_bytes() of the same problem is an upper bound.  Larger
  * problems get ESA_ERR_SCRATCH_LIMIT before anything is launched.  Example: B = 256,
  * T = 8192, H = 8, Dh = 64 in fp16 needs 64 MiB + 256 bytes and is refused; T = 4096 fits.

@@ -48,6 +48,18 @@ def test_random_case(seed):
     run_case(seed, case_of(seed))
 
 
+# fp16, Dh = 64 sizes in the forward's tile table (256-thread workgroups), with random draws
+TABLE_CASES = [(1, 700, 8), (4, 512, 8), (4, 333, 8), (1, 2000, 8), (16, 1024, 32), (2, 900, 16)]
+
+
+@pytest.mark.parametrize("k", range(len(TABLE_CASES)))
+def test_random_case_tile_table(k):
+    B, T, H = TABLE_CASES[k]
+    c = case_of(20_000 + k)
+    c.update(B=B, T=T, H=H, Dh=64, dtype=torch.float16)
+    run_case(20_000 + k, c)
+
+
 @pytest.mark.parametrize("seed", range(48))
 def test_random_case_retentive(seed):
     run_case(10_000 + seed, retentive_case_of(seed))

@@ -76,6 +76,10 @@ SHAPES = [
     (4, 130, 4, 32),
     (2, 200, 8, 128),
     (16, 257, 2, 16),
+    # fp16, Dh = 64 sizes that the forward's tile table gives 256-thread workgroups (128-step
+    # tiles): 8 channel blocks at T = 1024, and a ragged T = 1000 of 8 blocks
+    (1, 1024, 8, 64),
+    (2, 1000, 4, 64),
 ]
 DTYPE_MODE = [("f32", "direct"), ("f32", "controlled"), ("f16", "controlled"), ("f16", "direct"),
               ("bf16", "direct"), ("bf16", "controlled"), ("f8e4m3", "controlled"),
