@@ -26,7 +26,7 @@ namespace esa {
 template <typename T, int MODE, int DH, int L, int NT, bool GRADS, bool FULL, int CHAIN>
 __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint32_t cb,
                                          Acc<T>* sP, Acc<T>* sE, Acc<T>* sWP, Acc<T>* sWE,
-                                         Acc<T>* sCarry) {
+                                         Acc<T>* sCarry, float* sGate) {
     using G = Geom<T, DH, L, NT>;
     constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, HL = G::HL;
     constexpr int TT = G::TT;
@@ -103,6 +103,13 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         }
     }
 
+    // one-byte storage: the gate table (kGateTable), filled while the loads are in flight
+    constexpr bool TAB = kGateTable<T> && FULL;
+    if constexpr (TAB) {
+        fill_gate_table<T, NT>(sGate);
+        __syncthreads();
+    }
+
     // ---- gates and the thread's forward fold ----
     // S_[i][e] = 1 - s (the complement, GP); V_[i][e] = v (masked steps: 0 and 0, the
     // identity); with fp32 storage also U_[i][e] = s (1 - s) (gate_u_slope)
@@ -118,7 +125,10 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
     for (int i = 0; i < L; ++i) {
         const bool ok = FULL || (lane_ok && t0 + i < p.T);
         float av[VEC];
-        unpack<T>(ra[i], av);
+        if constexpr (TAB)
+            gate_u_lookup(ra[i], sGate, av);
+        else
+            unpack<T>(ra[i], av);
         unpack<T>(rv[i], V_[i]);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
@@ -128,7 +138,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
                 u = gate_u_slope(av[e], su);
                 U_[i][e] = ok ? su : 0.0f;
             } else {
-                u = gate_u(av[e]);
+                u = TAB ? av[e] : gate_u(av[e]);
             }
             S_[i][e] = ok ? u : 0.0f;
             V_[i][e] = ok ? V_[i][e] : 0.0f;
@@ -287,6 +297,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     __shared__ F sWP[NW * CB];  // per-wave aggregates
     __shared__ F sWE[NW * CB];
     __shared__ F sCarry[CB];
+    float* sGate = nullptr;
+    if constexpr (kGateTable<T>) {
+        __shared__ float gateTable[256];
+        sGate = gateTable;
+    }
 
     uint32_t rtile, cb;
     tile_of(blockIdx.x, p.nCB, rtile, cb);
@@ -296,9 +311,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     const bool full = (int64_t)(tile + 1) * TT <= p.T && (int64_t)(cb + 1) * CB <= p.nLanes &&
                       p.C % CB == 0 && (int64_t)TT * p.C * (int64_t)sizeof(T) < (int64_t(1) << 31);
     if (full)
-        bwd_tile<T, MODE, DH, L, NT, GRADS, true, CHAIN>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
+        bwd_tile<T, MODE, DH, L, NT, GRADS, true, CHAIN>(p, tile, cb, sP, sE, sWP, sWE, sCarry,
+                                                         sGate);
     else
-        bwd_tile<T, MODE, DH, L, NT, GRADS, false, CHAIN>(p, tile, cb, sP, sE, sWP, sWE, sCarry);
+        bwd_tile<T, MODE, DH, L, NT, GRADS, false, CHAIN>(p, tile, cb, sP, sE, sWP, sWE, sCarry,
+                                                          sGate);
 }
 
 template <typename T, int MODE, int DH, int CHAIN>

@@ -456,6 +456,30 @@ __device__ __forceinline__ float gate_u(float a) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * 1.4426950408889634f));
 }
 __device__ __forceinline__ float gate_slope(float u) { return __builtin_fmaf(-u, u, u); }
+
+// One-byte storage has only 256 logit codes: the scans evaluate gate_u once per code into a
+// table in LDS at the start of a workgroup and look every step's complement up there, one
+// byte extraction and one LDS read in place of the decode, exponential, add and reciprocal.
+// The table holds gate_u of the decoded code, so the values are the same bits as evaluated
+// in place.
+template <typename T>
+constexpr bool kGateTable = sizeof(T) == 1;
+template <typename T, int NT>
+__device__ __forceinline__ void fill_gate_table(float* tab) {
+    for (int i = threadIdx.x; i < 256; i += NT) {
+        float a[Storage<T>::VEC];
+        unpack<T>(make_uint4((uint32_t)i, 0u, 0u, 0u), a);
+        tab[i] = gate_u(a[0]);
+    }
+}
+// The complements of a thread's 8 one-byte logits (words x, y; byte k = element k).
+__device__ __forceinline__ void gate_u_lookup(const uint4& r, const float* tab, float* u) {
+    const uint32_t w[2] = {r.x, r.y};
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[4 * k + e] = tab[(w[k] >> (8 * e)) & 0xffu];
+}
 // The same complement with the derivative s (1 - s) = exp(a) u^2 to full relative precision,
 // for fp32 storage, whose bar would see the absolute error of u - u^2 where s is small.
 // exp(a) is capped at 2^126 so that s (1 - s) is 0, not NaN, where it overflows (u is 0

@@ -20,7 +20,7 @@ template <typename T, int MODE, int DH, int L, int NT, bool READOUT, bool PROD, 
           int CHAIN>
 __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint32_t cb,
                                          Acc<T>* sP, Acc<T>* sE, Acc<T>* sWP, Acc<T>* sWE,
-                                         Acc<T>* sCarry) {
+                                         Acc<T>* sCarry, float* sGate) {
     using G = Geom<T, DH, L, NT>;
     constexpr int VEC = G::VEC, CB = G::CB, NCL = G::NCL, HL = G::HL;
     constexpr int TT = G::TT;
@@ -79,11 +79,19 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         }
     }
 
+    // one-byte storage: the gate table (kGateTable), filled while the loads are in flight
+    constexpr bool TAB = kGateTable<T>;
+    if constexpr (TAB) {
+        fill_gate_table<T, NT>(sGate);
+        __syncthreads();
+    }
+
     // ---- level 1: gates and the thread's own fold (identity step where masked) ----
     // Each step is x' = s x + b (update()).  With fp32 accumulation SB[i] holds s = 1 - u and
     // WB[i] the write term b, so the re-run below is one fma per step; with fp64 accumulation
     // they hold u and v, and s and b are formed in fp64 at each use (an fp32 s would round).
-    // A masked step holds s = 1, b = 0 (u = 0, v = 0).
+    // A masked step holds s = 1, b = 0 (u = 0, v = 0).  One-byte storage does not keep them
+    // (REDO below).
     constexpr bool WIDE = std::is_same<F, double>::value;
     float SB[L][VEC], WB[L][VEC];
     F P[VEC], E[VEC];
@@ -96,11 +104,14 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
     for (int i = 0; i < L; ++i) {
         const bool ok = FULL || (lane_ok && t0 + i < p.T);
         float av[VEC], vv[VEC];
-        unpack<T>(ra[i], av);
+        if constexpr (TAB)
+            gate_u_lookup(ra[i], sGate, av);
+        else
+            unpack<T>(ra[i], av);
         unpack<T>(rv[i], vv);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const float u = ok ? gate_u(av[e]) : 0.0f;
+            const float u = ok ? (TAB ? av[e] : gate_u(av[e])) : 0.0f;
             const float v = ok ? vv[e] : 0.0f;
             const F s = F(1) - F(u), b = step_b<MODE, F>(F(u), F(v));
             SB[i][e] = WIDE ? u : float(s);
@@ -194,14 +205,34 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         for (int e = 0; e < VEC; ++e) E[e] = Q::comp(XP[e], F(sCarry[j * VEC + e]), XE[e]);
     }
     const int64_t ckbase = b * p.nck;
+    // One-byte storage re-derives each step's s and b from the raw words through the gate
+    // table instead of keeping SB and WB: 77 rather than 112 VGPRs, three workgroups per CU
+    // rather than two, and the same values (the table holds gate_u of each code, and s and b
+    // are formed as in the fold).  The empty asm hides the words' values from the compiler,
+    // which would otherwise keep the fold's results alive instead of recomputing them.
+    constexpr bool REDO = TAB && !WIDE;
+    if constexpr (REDO) {
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+            asm volatile("" : "+v"(ra[i].x), "+v"(ra[i].y), "+v"(ra[i].z), "+v"(ra[i].w),
+                              "+v"(rv[i].x), "+v"(rv[i].y), "+v"(rv[i].z), "+v"(rv[i].w));
+    }
 #pragma unroll
     for (int i = 0; i < L; ++i) {
         const int64_t t = t0 + i;
         const bool ok = FULL || (lane_ok && t < p.T);
         float ss = 0.0f, Ef[VEC];
+        float ru[VEC], rw[VEC];
+        if constexpr (REDO) {
+            gate_u_lookup(ra[i], sGate, ru);
+            unpack<T>(rv[i], rw);
+        }
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            if constexpr (WIDE)
+            if constexpr (REDO) {
+                const float u = ok ? ru[e] : 0.0f, v = ok ? rw[e] : 0.0f;
+                E[e] = update<F>(E[e], F(1) - F(u), step_b<MODE, F>(F(u), F(v)));
+            } else if constexpr (WIDE)
                 E[e] = update<F>(E[e], F(1) - F(SB[i][e]), step_b<MODE, F>(F(SB[i][e]), F(WB[i][e])));
             else
                 E[e] = update<F>(E[e], F(SB[i][e]), F(WB[i][e]));
@@ -246,6 +277,11 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
     __shared__ F sWP[NW * CB];  // per-wave aggregate pairs
     __shared__ F sWE[NW * CB];
     __shared__ F sCarry[CB];
+    float* sGate = nullptr;
+    if constexpr (kGateTable<T>) {
+        __shared__ float gateTable[256];
+        sGate = gateTable;
+    }
 
     uint32_t tile, cb;
     tile_of(blockIdx.x, p.nCB, tile, cb);
@@ -255,10 +291,10 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdParams p) {
                       p.C % CB == 0 && (int64_t)TT * p.C * (int64_t)sizeof(T) < (int64_t(1) << 31);
     if (full)
         fwd_tile<T, MODE, DH, L, NT, READOUT, PROD, true, CHAIN>(p, tile, cb, sP, sE, sWP, sWE,
-                                                                 sCarry);
+                                                                 sCarry, sGate);
     else
         fwd_tile<T, MODE, DH, L, NT, READOUT, PROD, false, CHAIN>(p, tile, cb, sP, sE, sWP, sWE,
-                                                                  sCarry);
+                                                                  sCarry, sGate);
 }
 
 template <typename T, int MODE, int DH, int CHAIN, int V = 0>
