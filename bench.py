@@ -557,6 +557,8 @@ def main():
     result = {"metric": "scan fwd+bwd tokens/s and % of HBM peak at 64K ctx; decode steps/s",
               "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+              # dtype: the type the path computes in (fp32 arithmetic and states); the
+              # storage type of the sequences (fp16) is config["storage"]
               "scaling": "weak", "vs_baseline": None, "dtype": "f32",
               "data": "synthetic (seeded N(mu, sigma) draws shaped like the pages' workloads)"}
     train = None
