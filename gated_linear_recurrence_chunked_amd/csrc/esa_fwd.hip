@@ -210,12 +210,15 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
     // rather than two, and the same values (the table holds gate_u of each code, and s and b
     // are formed as in the fold).  The empty asm hides the words' values from the compiler,
     // which would otherwise keep the fold's results alive instead of recomputing them.
+    // One statement over the four steps' words (words x, y: the upper two of a one-byte
+    // load are zero): per-step statements compiled to 103 VGPRs.
     constexpr bool REDO = TAB && !WIDE;
     if constexpr (REDO) {
-#pragma unroll
-        for (int i = 0; i < L; ++i)
-            asm volatile("" : "+v"(ra[i].x), "+v"(ra[i].y), "+v"(ra[i].z), "+v"(ra[i].w),
-                              "+v"(rv[i].x), "+v"(rv[i].y), "+v"(rv[i].z), "+v"(rv[i].w));
+        static_assert(L == 4, "the re-derived steps hide four steps' words in one statement");
+        asm volatile("" : "+v"(ra[0].x), "+v"(ra[0].y), "+v"(rv[0].x), "+v"(rv[0].y),
+                          "+v"(ra[1].x), "+v"(ra[1].y), "+v"(rv[1].x), "+v"(rv[1].y),
+                          "+v"(ra[2].x), "+v"(ra[2].y), "+v"(rv[2].x), "+v"(rv[2].y),
+                          "+v"(ra[3].x), "+v"(ra[3].y), "+v"(rv[3].x), "+v"(rv[3].y));
     }
 #pragma unroll
     for (int i = 0; i < L; ++i) {
