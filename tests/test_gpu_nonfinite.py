@@ -4,8 +4,8 @@ the slot scan and the look-back.
 Under E_t = s_t E_{t-1} + B_t (page "entangled-state-attention 0.1.0", "Core idea") a NaN
 gate or value at step t0 makes its lane NaN from t0 on (0 * NaN is NaN); a NaN query
 poisons only that readout, and in the backward every gradient of its head at and before
-t0.  A logit of +inf gives the gate 1 exactly; -inf gives a gate of 0 (the kernels use
-2^-126).  The oracle follows the same definition in fp64, so NaN positions must agree
+t0.  A logit of +inf gives the gate 1 exactly and -inf the gate 0 exactly (the complement
+1 / (1 + e^a) is 0 and 1).  The oracle follows the same definition in fp64, so NaN positions must agree
 exactly and the finite values within the parity bar.
 """
 import sys
@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from gated_linear_recurrence_chunked_amd import binding, synth
-from helpers import TOL, err, f64
+from helpers import FLOOR, TOL, err, f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -35,7 +35,7 @@ def same_nan_then_close(name, got, ref, dtype):
     fin = ~rn
     assert np.array_equal(np.isinf(g[fin]), np.isinf(r[fin])), f"{name}: inf pattern differs"
     ok = fin & np.isfinite(r)
-    e = err(g[ok], r[ok])
+    e = err(g[ok], r[ok], FLOOR.get(dtype, 0.0))
     print(f"  {name}: {rn.sum()} NaN, err {e:.3e} on the rest", flush=True)
     assert e <= TOL[dtype], f"{name}: err {e:.3e}"
 
@@ -51,7 +51,12 @@ CASES = {
 
 
 @pytest.mark.parametrize("case", list(CASES))
-@pytest.mark.parametrize("dt,mode", [(torch.float16, "controlled"), (torch.float32, "direct")])
+# One-byte storage takes its gates from a table of the 256 codes, whose NaN (and E5M2
+# infinity) codes must give what the gate gives in place.  E4M3 has no infinity: an infinite
+# logit is stored as NaN, and the oracle reads the same stored codes.
+@pytest.mark.parametrize("dt,mode", [(torch.float16, "controlled"), (torch.float32, "direct"),
+                                     (torch.float8_e4m3fn, "controlled"),
+                                     (torch.float8_e5m2, "direct")])
 def test_nonfinite_inputs_follow_the_definition(case, dt, mode):
     B, T, H, Dh = 2, 2000, 2, 64  # 8 forward and 16 backward tiles per channel block
     say(f"non-finite {case} {dt} {mode}")
@@ -71,7 +76,7 @@ def test_nonfinite_inputs_follow_the_definition(case, dt, mode):
     ry, reT = oracle.scan_fwd(x["a"], x["v"], x["q"], e0, mode=m, threads=2)
     rda, rdv, rdq, rde0 = oracle.scan_bwd(x["a"], x["v"], x["q"], x["dy"], e0, None, mode=m,
                                           threads=2)
-    state_dt = torch.float16 if dt == torch.float16 else torch.float32
+    state_dt = torch.float32  # the fp32 outputs of every storage meet the fp32 bar
     same_nan_then_close("y", y, ry, dt)
     same_nan_then_close("final_state", eT, reT, state_dt)
     same_nan_then_close("d_logit", da, rda, dt)
