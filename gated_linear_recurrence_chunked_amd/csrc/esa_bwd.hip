@@ -103,7 +103,9 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, uint32_t tile, uint
         }
     }
 
-    // one-byte storage: the gate table (kGateTable), filled while the loads are in flight
+    // one-byte storage, full tiles: the gate table (kGateTable), filled while the loads are in
+    // flight (ragged tiles evaluate the gate in place: there the table raised the kernel's
+    // register peak from 232 to 265 VGPRs, one wave per SIMD)
     constexpr bool TAB = kGateTable<T> && FULL;
     if constexpr (TAB) {
         fill_gate_table<T, NT>(sGate);

@@ -205,13 +205,15 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         for (int e = 0; e < VEC; ++e) E[e] = Q::comp(XP[e], F(sCarry[j * VEC + e]), XE[e]);
     }
     const int64_t ckbase = b * p.nck;
-    // One-byte storage re-derives each step's s and b from the raw words through the gate
-    // table instead of keeping SB and WB: 77 rather than 112 VGPRs, three workgroups per CU
-    // rather than two, and the same values (the table holds gate_u of each code, and s and b
-    // are formed as in the fold).  The empty asm hides the words' values from the compiler,
-    // which would otherwise keep the fold's results alive instead of recomputing them.
-    // One statement over the four steps' words (words x, y: the upper two of a one-byte
-    // load are zero): per-step statements compiled to 103 VGPRs.
+    // One-byte storage re-derives each step's gate from the raw words through the gate table
+    // instead of keeping SB and WB: 77 rather than 112 VGPRs, three workgroups per CU rather
+    // than two.  This forward is bound by its vector ALU, so the controlled step takes the
+    // two-instruction form E + u (v - E), equal to s E + u v up to rounding: one rounding of
+    // v - E, scaled by u, and one of the result (E, a convex combination of the initial state
+    // and the values, keeps v - E on their scale).  The empty asm hides the words' values
+    // from the compiler, which would otherwise keep the fold's results alive instead of
+    // recomputing them; one statement covers the four steps' words (words x, y: the upper two
+    // of a one-byte load are zero), as per-step statements compiled to 103 VGPRs.
     constexpr bool REDO = TAB && !WIDE;
     if constexpr (REDO) {
         static_assert(L == 4, "the re-derived steps hide four steps' words in one statement");
@@ -234,7 +236,10 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, uint32_t tile, uint
         for (int e = 0; e < VEC; ++e) {
             if constexpr (REDO) {
                 const float u = ok ? ru[e] : 0.0f, v = ok ? rw[e] : 0.0f;
-                E[e] = update<F>(E[e], F(1) - F(u), step_b<MODE, F>(F(u), F(v)));
+                if constexpr (MODE == kControlled)
+                    E[e] = fma_(F(u), F(v) - E[e], E[e]);
+                else
+                    E[e] = update<F>(E[e], F(1) - F(u), F(v));
             } else if constexpr (WIDE)
                 E[e] = update<F>(E[e], F(1) - F(SB[i][e]), step_b<MODE, F>(F(SB[i][e]), F(WB[i][e])));
             else
