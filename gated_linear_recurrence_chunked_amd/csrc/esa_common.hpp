@@ -355,18 +355,21 @@ __device__ __forceinline__ uint4 pack<__bf16>(const float* x) {
 }
 
 // Out-of-range values follow the formats' own conversion: NaN for E4M3 beyond 464 in
-// magnitude, infinity for E5M2 beyond 61440.
+// magnitude, infinity for E5M2 beyond 61440.  The first conversion of a word fills its low
+// half and keeps the high half of its `old` operand, which the second one then overwrites:
+// `old` is given the first input's bits rather than 0, which would cost a move per word.
 template <bool E5M2>
 __device__ __forceinline__ uint4 pack_f8(const float* x) {
     uint32_t w[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         int v;
+        const int any = __float_as_int(x[4 * k]);
         if constexpr (E5M2) {
-            v = __builtin_amdgcn_cvt_pk_bf8_f32(x[4 * k], x[4 * k + 1], 0, false);
+            v = __builtin_amdgcn_cvt_pk_bf8_f32(x[4 * k], x[4 * k + 1], any, false);
             v = __builtin_amdgcn_cvt_pk_bf8_f32(x[4 * k + 2], x[4 * k + 3], v, true);
         } else {
-            v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k], x[4 * k + 1], 0, false);
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k], x[4 * k + 1], any, false);
             v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k + 2], x[4 * k + 3], v, true);
         }
         w[k] = (uint32_t)v;
