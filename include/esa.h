@@ -17,15 +17,18 @@
  * projection W_O are outside the library: it takes the gate logits, values and queries.
  *
  * Layout.  Sequence tensors are contiguous [B, T, H, Dh] with Dh fastest, in the storage
- * dtype.  States are contiguous [B, H, Dh] and always fp32.  All arithmetic is fp32 with
- * fp32 accumulation; outputs in a 16- or 8-bit dtype are rounded to nearest even.  An 8-bit
+ * dtype.  States are contiguous [B, H, Dh] and always fp32.  Arithmetic is fp32, with fp64
+ * accumulation for fp32 storage (states, gradients and the scans' compositions; gates,
+ * readout and the cross-tile words stay fp32); outputs in a 16- or 8-bit dtype are rounded
+ * to nearest even.  An 8-bit
  * output beyond its format's range becomes what the format's conversion gives: NaN for E4M3
  * (magnitude at least 464), infinity for E5M2 (at least 61440).
  *
  * Ownership and execution.  The caller owns every buffer (device memory).  The library
- * never allocates, frees or synchronises; each call validates its arguments on the host,
- * enqueues its kernels on `stream` (a hipStream_t; NULL is the default stream) and
- * returns.  Errors that occur while the kernels run surface at the caller's next
+ * never allocates or frees; each call validates its arguments on the host, enqueues its
+ * kernels on `stream` (a hipStream_t; NULL is the default stream) and returns.  Two calls
+ * also wait for the stream: esa_workspace_status (to read the header) and the first call of
+ * esa_scan_fwd_noalloc on a device (which clears its static scratch once).  Errors that occur while the kernels run surface at the caller's next
  * synchronisation.  The library is reentrant; its only global state is a process-wide
  * counter that tags each scan launch's look-back words.  Calls that share one workspace
  * must not run concurrently (use one workspace per stream).
